@@ -1,0 +1,11 @@
+"""fp64 CPU oracle for Kimi Delta Attention -- test infrastructure only.
+
+Only ``tests/``, the smoke check and the benchmark's CPU-baseline leg use
+this package; the HIP library and its Python binding never import it.
+"""
+from .kda_oracle import (SOURCE, build, compile_source, load_library,
+                         run_decode, run_fixed, run_varlen, set_threads,
+                         threads)
+
+__all__ = ["SOURCE", "build", "compile_source", "load_library", "run_decode",
+           "run_fixed", "run_varlen", "set_threads", "threads"]
