@@ -1,0 +1,196 @@
+// C-ABI entry points of libkda (declared and documented in include/kda.h):
+// argument validation on the host, then kernel launches on the caller's
+// stream.  Validation touches no HIP API, so an invalid call returns before
+// anything is enqueued.
+#include "../../include/kda.h"
+
+#include <limits.h>
+
+#include "kda_internal.hpp"
+
+namespace {
+
+bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+bool supported_dims(int32_t Dk, int32_t Dv) {
+  return Dk == Dv && (Dk == 16 || Dk == 32 || Dk == 64 || Dk == 128);
+}
+
+bool supported_chunk(int32_t C) { return C == 16 || C == 32 || C == 64; }
+
+// Shape / dtype checks shared by both prefill entry points.
+kda_status_t check_prefill_common(int32_t H, int32_t Dk, int32_t Dv,
+                                  int32_t C, int32_t dtype) {
+  if (H <= 0 || Dk <= 0 || Dv <= 0 || C <= 0) return KDA_ERR_INVALID_ARG;
+  if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_FP32)
+    return KDA_ERR_UNSUPPORTED;
+  if (!supported_dims(Dk, Dv) || !supported_chunk(C))
+    return KDA_ERR_UNSUPPORTED;
+  if (H > 65535) return KDA_ERR_UNSUPPORTED;  // grid y of the prep launch
+  return KDA_OK;
+}
+
+kda_status_t run_prefill(kda::PrefillArgs& a, int32_t D, int32_t C,
+                         int32_t dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const size_t need = kda_prefill_workspace_size(a.N, a.total_T, a.H, D, D, C);
+  if (need == 0) return KDA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
+  a.ws = static_cast<char*>(workspace);
+  a.nslots = kda::num_slots(a.N, a.total_T, C);
+  const bool bf16_io = dtype == KDA_DTYPE_BF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.total_T > 0 && a.max_chunks > 0) {
+    if (kda::launch_prep(a, D, C, bf16_io, st) != hipSuccess)
+      return KDA_ERR_LAUNCH;
+  }
+  if (kda::launch_recur(a, D, C, bf16_io, st) != hipSuccess)
+    return KDA_ERR_LAUNCH;
+  return KDA_OK;
+}
+
+kda_status_t check_tensors(int64_t tokens, const void* q, const void* k,
+                           const void* v, const float* g, const float* beta,
+                           const void* o) {
+  if (tokens > 0) {
+    if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+        !aligned(g, 16) || !aligned(o, 16) || !aligned(beta, 4))
+      return KDA_ERR_INVALID_ARG;
+  }
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(int32_t status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_INVALID_ARG: return "invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "unsupported size, chunk or dtype";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t kda_prefill_workspace_size(int32_t N, int64_t total_T, int32_t H,
+                                  int32_t Dk, int32_t Dv, int32_t C) {
+  if (N <= 0 || total_T < 0 || H <= 0 || !supported_dims(Dk, Dv) ||
+      !supported_chunk(C))
+    return 0;
+  const kda::WsLayout lay = kda::WsLayout::make(C, Dk, Dv);
+  const int64_t slots = kda::num_slots(N, total_T, C);
+  return (size_t)slots * (size_t)H * lay.block_bytes;
+}
+
+kda_status_t kda_prefill_chunked(const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta,
+                                 const float* initial_state,
+                                 float* final_state, void* o, int32_t B,
+                                 int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                                 int32_t C, float scale, int32_t dtype,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (B <= 0 || T < 0) return KDA_ERR_INVALID_ARG;
+  kda_status_t st = check_prefill_common(H, Dk, Dv, C, dtype);
+  if (st != KDA_OK) return st;
+  if (B > 65535) return KDA_ERR_UNSUPPORTED;  // grid z of the prep launch
+  const int64_t total = (int64_t)B * T;
+  st = check_tensors(total, q, k, v, g, beta, o);
+  if (st != KDA_OK) return st;
+  if ((initial_state && !aligned(initial_state, 16)) ||
+      (final_state && !aligned(final_state, 16)))
+    return KDA_ERR_INVALID_ARG;
+  if ((int64_t)(Dv / (Dv >= 32 ? 32 : 16)) * H * B > INT_MAX)
+    return KDA_ERR_UNSUPPORTED;
+
+  kda::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.cu_seqlens = nullptr;
+  a.T_fixed = T;
+  a.N = B;
+  a.total_T = total;
+  a.max_chunks = (T + C - 1) / C;
+  a.initial_state = initial_state;
+  a.final_state = final_state;
+  a.o = o;
+  a.H = H;
+  a.scale = scale;
+  return run_prefill(a, Dk, C, dtype, workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_prefill_varlen(const void* q, const void* k, const void* v,
+                                const float* g, const float* beta,
+                                const int32_t* cu_seqlens, int32_t N,
+                                int64_t total_T, int32_t max_seqlen,
+                                const float* initial_state,
+                                float* final_state, void* o, int32_t H,
+                                int32_t Dk, int32_t Dv, int32_t C, float scale,
+                                int32_t dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (N <= 0 || total_T < 0 || max_seqlen < 0) return KDA_ERR_INVALID_ARG;
+  if (total_T > 0 && max_seqlen == 0) return KDA_ERR_INVALID_ARG;
+  kda_status_t st = check_prefill_common(H, Dk, Dv, C, dtype);
+  if (st != KDA_OK) return st;
+  if (N > 65535) return KDA_ERR_UNSUPPORTED;
+  if (!cu_seqlens || !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARG;
+  st = check_tensors(total_T, q, k, v, g, beta, o);
+  if (st != KDA_OK) return st;
+  if ((initial_state && !aligned(initial_state, 16)) ||
+      (final_state && !aligned(final_state, 16)))
+    return KDA_ERR_INVALID_ARG;
+  if ((int64_t)(Dv / (Dv >= 32 ? 32 : 16)) * H * N > INT_MAX)
+    return KDA_ERR_UNSUPPORTED;
+  const int64_t maxlen = max_seqlen < total_T ? max_seqlen : total_T;
+
+  kda::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.cu_seqlens = cu_seqlens;
+  a.T_fixed = 0;
+  a.N = N;
+  a.total_T = total_T;
+  a.max_chunks = (int32_t)((maxlen + C - 1) / C);
+  a.initial_state = initial_state;
+  a.final_state = final_state;
+  a.o = o;
+  a.H = H;
+  a.scale = scale;
+  return run_prefill(a, Dk, C, dtype, workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_decode_step(const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, float* state,
+                             void* o, int32_t B, int32_t H, int32_t Dk,
+                             int32_t Dv, float scale, int32_t dtype,
+                             void* stream) {
+  if (B <= 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERR_INVALID_ARG;
+  if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_FP32)
+    return KDA_ERR_UNSUPPORTED;
+  if (!supported_dims(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > INT_MAX) return KDA_ERR_UNSUPPORTED;
+  kda_status_t st = check_tensors((int64_t)B, q, k, v, g, beta, o);
+  if (st != KDA_OK) return st;
+  if (!state || !aligned(state, 16)) return KDA_ERR_INVALID_ARG;
+
+  kda::DecodeArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.state = state;
+  a.o = o;
+  a.B = B;
+  a.H = H;
+  a.scale = scale;
+  if (kda::launch_decode(a, Dk, dtype == KDA_DTYPE_BF16,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KDA_ERR_LAUNCH;
+  return KDA_OK;
+}
+
+}  // extern "C"

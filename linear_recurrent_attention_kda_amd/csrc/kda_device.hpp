@@ -1,0 +1,113 @@
+// Device helpers shared by the libkda kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+// Storage types of q, k, v, o.
+template <typename T> struct io;
+template <> struct io<bf16> {
+  static __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+  static __device__ __forceinline__ bf16 from_f(float x) { return (bf16)x; }
+};
+template <> struct io<float> {
+  static __device__ __forceinline__ float to_f(float x) { return x; }
+  static __device__ __forceinline__ float from_f(float x) { return x; }
+};
+
+// Eight consecutive elements of a storage-dtype row as floats (16-byte
+// aligned for bf16, 32-byte for fp32).
+__device__ __forceinline__ void load8(const bf16* p, float (&x)[8]) {
+  const uint4 raw = *reinterpret_cast<const uint4*>(p);
+  const bf16x8 v = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
+}
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float (&x)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)x[i];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const bf16* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  return __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
+}
+
+// D += A(16x32) * B(32x16), bf16 operands, fp32 accumulate.  Lane l holds
+// row (l % 16) of A and column (l % 16) of B, each with the 8 contraction
+// indices of lane group l / 16 (the same indices for A and B); D element
+// (4 * (l / 16) + i, l % 16) is acc[i].
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
+// D += A(16x4) * B(4x16) in fp32.  Lane l holds A(l % 16, l / 16) and
+// B(l / 16, l % 16); D as above.
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Four consecutive storage-dtype elements (8-byte aligned for bf16, 16-byte
+// for fp32) from x * scale.
+__device__ __forceinline__ void store4(bf16* p, f32x4 x, float scale) {
+  bf16x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = (bf16)(x[i] * scale);
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void store4(float* p, f32x4 x, float scale) {
+  *reinterpret_cast<float4*>(p) =
+      make_float4(x[0] * scale, x[1] * scale, x[2] * scale, x[3] * scale);
+}
+
+}  // namespace kda
+
+#include "kda_internal.hpp"
+
+namespace kda {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Token range [bos, eos) of sequence n, clamped into [0, total_T] so that an
+// invalid cu_seqlens can never index outside the packed tensors.
+__device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int n,
+                                           int64_t& bos, int64_t& eos) {
+  if (a.cu_seqlens) {
+    int64_t b = a.cu_seqlens[n], e = a.cu_seqlens[n + 1];
+    b = b < 0 ? 0 : (b > a.total_T ? a.total_T : b);
+    e = e < b ? b : (e > a.total_T ? a.total_T : e);
+    bos = b;
+    eos = e;
+  } else {
+    bos = (int64_t)n * a.T_fixed;
+    eos = bos + a.T_fixed;
+  }
+}
+
+}  // namespace kda

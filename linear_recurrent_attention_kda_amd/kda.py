@@ -1,0 +1,242 @@
+"""Thin ctypes binding of libkda (include/kda.h), with the same entry-point
+names.  It only marshals arguments: checks tensor shapes, dtypes and
+devices, allocates outputs and the workspace with torch when the caller
+does not pass them, and hands raw device pointers and the current HIP stream
+to the library.  Every step of the computation runs in libkda's kernels; if
+the library is missing this module raises, it never falls back to anything
+else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("KDA_LIB", os.path.join(_PKG, "libkda.so"))
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "kda.h")
+
+KDA_OK = 0
+KDA_DTYPE_BF16 = 0
+KDA_DTYPE_FP32 = 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s (status %d)" %
+                         (fn, kda_status_string(status), status))
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libkda.so (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libkda.so not found at %s; build it with "
+                "`python -m linear_recurrent_attention_kda_amd.build`" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32,
+                                 ctypes.c_int64, ctypes.c_float,
+                                 ctypes.c_size_t)
+        lib.kda_abi_version.restype = i32
+        lib.kda_abi_version.argtypes = []
+        lib.kda_status_string.restype = ctypes.c_char_p
+        lib.kda_status_string.argtypes = [i32]
+        lib.kda_prefill_workspace_size.restype = sz
+        lib.kda_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32]
+        lib.kda_prefill_chunked.restype = i32
+        lib.kda_prefill_chunked.argtypes = [
+            vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+            i32, vp, sz, vp]
+        lib.kda_prefill_varlen.restype = i32
+        lib.kda_prefill_varlen.argtypes = [
+            vp, vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, i32,
+            i32, f32, i32, vp, sz, vp]
+        lib.kda_decode_step.restype = i32
+        lib.kda_decode_step.argtypes = [
+            vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
+        _lib = lib
+        return lib
+
+
+def declared_functions(header: str = HEADER):
+    """Names of the functions include/kda.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+# ---------------------------------------------------------------------------
+def kda_abi_version() -> int:
+    return int(load().kda_abi_version())
+
+
+def kda_status_string(status: int) -> str:
+    return load().kda_status_string(int(status)).decode()
+
+
+def kda_prefill_workspace_size(N: int, total_T: int, H: int, Dk: int,
+                               Dv: int, C: int) -> int:
+    return int(load().kda_prefill_workspace_size(N, total_T, H, Dk, Dv, C))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return KDA_DTYPE_FP32
+    raise TypeError("q, k, v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype, device):
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" %
+                         (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def workspace_for(N, total_T, H, Dk, Dv, C, device) -> torch.Tensor:
+    n = kda_prefill_workspace_size(N, total_T, H, Dk, Dv, C)
+    if n == 0:
+        raise ValueError("unsupported prefill sizes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def kda_prefill_chunked(q, k, v, g, beta, initial_state=None, *,
+                        chunk_size: int = 64, scale: float = 1.0,
+                        output_final_state: bool = True, final_state=None,
+                        o=None, workspace=None):
+    """Chunked prefill of a fixed-length batch.
+
+    q, k, g: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H] (q, k, v bf16
+    or fp32; g, beta fp32); initial_state: [B, H, Dk, Dv] fp32 or None.
+    Returns (o [B, T, H, Dv], final_state [B, H, Dk, Dv] fp32 or None).
+    final_state may be initial_state itself (updated in place).
+    """
+    lib = load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    for t, n, s, dt in ((q, "q", (B, T, H, Dk), q.dtype),
+                        (k, "k", (B, T, H, Dk), q.dtype),
+                        (v, "v", (B, T, H, Dv), q.dtype),
+                        (g, "g", (B, T, H, Dk), torch.float32),
+                        (beta, "beta", (B, T, H), torch.float32)):
+        _check(t, n, s, dt, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (B, H, Dk, Dv), torch.float32,
+               dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32,
+                                  device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (B, H, Dk, Dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev)
+    _check(o, "o", (B, T, H, Dv), q.dtype, dev)
+    if workspace is None:
+        workspace = workspace_for(B, B * T, H, Dk, Dv, chunk_size, dev)
+    st = lib.kda_prefill_chunked(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+        _ptr(final_state), _ptr(o), B, T, H, Dk, Dv, chunk_size, scale,
+        _dtype_code(q), _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_prefill_chunked", st)
+    return o, final_state
+
+
+def kda_prefill_varlen(q, k, v, g, beta, cu_seqlens, max_seqlen: int,
+                       initial_state=None, *, chunk_size: int = 64,
+                       scale: float = 1.0, output_final_state: bool = True,
+                       final_state=None, o=None, workspace=None):
+    """Chunked prefill of N packed sequences (append-prefill when an initial
+    state is given).
+
+    q, k, g: [total_T, H, Dk]; v: [total_T, H, Dv]; beta: [total_T, H];
+    cu_seqlens: int32 [N+1] on the device; max_seqlen: host int >= every
+    length; initial_state: [N, H, Dk, Dv] fp32 or None.
+    Returns (o [total_T, H, Dv], final_state [N, H, Dk, Dv] or None).
+    """
+    lib = load()
+    total_T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    N = cu_seqlens.numel() - 1
+    for t, n, s, dt in ((q, "q", (total_T, H, Dk), q.dtype),
+                        (k, "k", (total_T, H, Dk), q.dtype),
+                        (v, "v", (total_T, H, Dv), q.dtype),
+                        (g, "g", (total_T, H, Dk), torch.float32),
+                        (beta, "beta", (total_T, H), torch.float32),
+                        (cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)):
+        _check(t, n, s, dt, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (N, H, Dk, Dv), torch.float32,
+               dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32,
+                                  device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (N, H, Dk, Dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((total_T, H, Dv), dtype=q.dtype, device=dev)
+    _check(o, "o", (total_T, H, Dv), q.dtype, dev)
+    if workspace is None:
+        workspace = workspace_for(N, total_T, H, Dk, Dv, chunk_size, dev)
+    st = lib.kda_prefill_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N,
+        total_T, int(max_seqlen), _ptr(initial_state), _ptr(final_state),
+        _ptr(o), H, Dk, Dv, chunk_size, scale, _dtype_code(q),
+        _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_prefill_varlen", st)
+    return o, final_state
+
+
+def kda_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, o=None):
+    """One decode token per sequence; `state` [B, H, Dk, Dv] fp32 is updated
+    in place.  q, k, g: [B, H, Dk]; v: [B, H, Dv]; beta: [B, H].
+    Returns o [B, H, Dv]."""
+    lib = load()
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    for t, n, s, dt in ((q, "q", (B, H, Dk), q.dtype),
+                        (k, "k", (B, H, Dk), q.dtype),
+                        (v, "v", (B, H, Dv), q.dtype),
+                        (g, "g", (B, H, Dk), torch.float32),
+                        (beta, "beta", (B, H), torch.float32),
+                        (state, "state", (B, H, Dk, Dv), torch.float32)):
+        _check(t, n, s, dt, dev)
+    if o is None:
+        o = torch.empty((B, H, Dv), dtype=q.dtype, device=dev)
+    _check(o, "o", (B, H, Dv), q.dtype, dev)
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(state), _ptr(o), B, H, Dk, Dv, scale,
+                             _dtype_code(q), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_decode_step", st)
+    return o

@@ -1,0 +1,124 @@
+"""libkda's C ABI on the CPU: the library loads, exports every function that
+include/kda.h declares, and rejects bad arguments with the documented status
+before anything is enqueued.  No call here passes validation, so nothing is
+ever launched (there is no GPU in this environment)."""
+import ctypes
+import os
+
+import pytest
+
+from linear_recurrent_attention_kda_amd import kda
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kda.LIB_PATH),
+                                reason="libkda.so not built")
+
+OK, INVALID, UNSUP, WS = 0, -1, -2, -3
+P = ctypes.c_void_p(0x100000)          # a non-NULL, 256-aligned fake address
+MIS = ctypes.c_void_p(0x100002)        # misaligned
+NULL = None
+
+
+def test_exports_every_declared_symbol():
+    lib = kda.load()
+    names = kda.declared_functions()
+    assert set(names) == {"kda_abi_version", "kda_status_string",
+                          "kda_prefill_workspace_size", "kda_prefill_chunked",
+                          "kda_prefill_varlen", "kda_decode_step"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert kda.kda_abi_version() == 1
+    assert kda.kda_status_string(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert kda.kda_status_string(s) not in ("ok", "unknown status")
+    assert kda.kda_status_string(7) == "unknown status"
+
+
+def test_workspace_size_formula():
+    # per (head, slot) block: 3*C*Dk*2 + C*Dv*2 + C*C*2 + Dk*4, 256-aligned
+    C, D, H = 64, 128, 96
+    block = 3 * C * D * 2 + C * D * 2 + C * C * 2 + D * 4
+    block = (block + 255) // 256 * 256
+    assert kda.kda_prefill_workspace_size(1, 8192, H, D, D, C) == \
+        (8192 // C + 1) * H * block
+    assert kda.kda_prefill_workspace_size(8, 1000, 4, D, D, C) == \
+        (1000 // C + 8) * 4 * block
+    assert kda.kda_prefill_workspace_size(1, 10, 1, 96, 96, 64) == 0
+    assert kda.kda_prefill_workspace_size(1, 10, 1, 128, 128, 48) == 0
+    assert kda.kda_prefill_workspace_size(0, 10, 1, 128, 128, 64) == 0
+
+
+def _decode(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, state=P, o=P, B=2, H=2, Dk=128,
+             Dv=128, scale=1.0, dtype=0, stream=NULL)
+    a.update(kw)
+    return lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"],
+                               a["state"], a["o"], a["B"], a["H"], a["Dk"],
+                               a["Dv"], a["scale"], a["dtype"], a["stream"])
+
+
+def test_decode_validation():
+    lib = kda.load()
+    assert _decode(lib, B=0) == INVALID
+    assert _decode(lib, H=-1) == INVALID
+    assert _decode(lib, Dk=96, Dv=96) == UNSUP
+    assert _decode(lib, Dk=128, Dv=64) == UNSUP
+    assert _decode(lib, dtype=7) == UNSUP
+    assert _decode(lib, q=NULL) == INVALID
+    assert _decode(lib, state=NULL) == INVALID
+    assert _decode(lib, o=MIS) == INVALID
+    assert _decode(lib, state=MIS) == INVALID
+
+
+def _chunked(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, s0=NULL, s1=NULL, o=P, B=1, T=128,
+             H=2, Dk=128, Dv=128, C=64, scale=1.0, dtype=0, ws=P,
+             ws_bytes=1 << 40, stream=NULL)
+    a.update(kw)
+    return lib.kda_prefill_chunked(
+        a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["s1"], a["o"],
+        a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["C"], a["scale"],
+        a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_prefill_chunked_validation():
+    lib = kda.load()
+    assert _chunked(lib, B=0) == INVALID
+    assert _chunked(lib, T=-1) == INVALID
+    assert _chunked(lib, C=48) == UNSUP
+    assert _chunked(lib, C=128) == UNSUP
+    assert _chunked(lib, Dk=256, Dv=256) == UNSUP
+    assert _chunked(lib, dtype=3) == UNSUP
+    assert _chunked(lib, g=NULL) == INVALID
+    assert _chunked(lib, k=MIS) == INVALID
+    assert _chunked(lib, s0=MIS) == INVALID
+    assert _chunked(lib, ws=NULL) == WS
+    assert _chunked(lib, ws_bytes=1000) == WS
+    assert _chunked(lib, ws=ctypes.c_void_p(0x100010)) == INVALID
+
+
+def _varlen(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, cu=P, N=2, total=100, maxlen=64,
+             s0=NULL, s1=NULL, o=P, H=2, Dk=64, Dv=64, C=64, scale=1.0,
+             dtype=0, ws=P, ws_bytes=1 << 40, stream=NULL)
+    a.update(kw)
+    return lib.kda_prefill_varlen(
+        a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"],
+        a["total"], a["maxlen"], a["s0"], a["s1"], a["o"], a["H"], a["Dk"],
+        a["Dv"], a["C"], a["scale"], a["dtype"], a["ws"], a["ws_bytes"],
+        a["stream"])
+
+
+def test_prefill_varlen_validation():
+    lib = kda.load()
+    assert _varlen(lib, N=0) == INVALID
+    assert _varlen(lib, cu=NULL) == INVALID
+    assert _varlen(lib, cu=ctypes.c_void_p(0x100001)) == INVALID
+    assert _varlen(lib, maxlen=-1) == INVALID
+    assert _varlen(lib, maxlen=0) == INVALID
+    assert _varlen(lib, total=-5) == INVALID
+    assert _varlen(lib, C=8) == UNSUP
+    assert _varlen(lib, ws_bytes=10) == WS
+    assert _varlen(lib, v=NULL) == INVALID

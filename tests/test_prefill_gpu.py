@@ -1,0 +1,125 @@
+"""GPU parity of kda_prefill_chunked / kda_prefill_varlen against the fp64
+oracle (through the C ABI).
+
+Small cases span several chunks, a ragged tail and every supported head dim
+and chunk size, and are compared completely.  The full-size workloads are
+run in the launch configuration the benchmark times and compared on sampled
+heads, which the oracle computes one by one (heads are independent)."""
+import numpy as np
+import pytest
+import torch
+
+from conftest import gpu_available
+from linear_recurrent_attention_kda_amd import inputs, kda
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+import gpu_util as U  # noqa: E402
+
+
+def test_tiny_workload():
+    """B=1, H=2, T=64, d=16, C=16, fp32, zero state, seed 0."""
+    U.check_prefill(inputs.make("tiny", seed=0))
+
+
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+@pytest.mark.parametrize("C", [16, 32, 64])
+def test_dims_and_chunks(D, C):
+    p = inputs.make("prefill", seed=D + C, B=1, T=203, H=3, K=D, V=D, C=C,
+                    s0=True)
+    U.check_prefill(p, label="D%d C%d" % (D, C))
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 64, 65, 129])
+def test_lengths_around_chunk_edges(T):
+    p = inputs.make("prefill", seed=T, B=2, T=T, H=2, s0=True)
+    U.check_prefill(p, label="T%d" % T)
+
+
+def test_fp32_io():
+    p = inputs.make("prefill", seed=4, B=1, T=300, H=2, dtype="fp32", s0=True)
+    U.check_prefill(p, label="fp32")
+
+
+@pytest.mark.parametrize("case", ["g_min", "g_zero", "beta0", "beta1"])
+def test_edge_values(case):
+    kw = dict(g_min=dict(g_const=-5.0), g_zero=dict(g_const=0.0),
+              beta0=dict(beta_const=0.0), beta1=dict(beta_const=1.0))[case]
+    p = inputs.make("prefill", seed=21, B=1, T=260, H=2, s0=True, **kw)
+    U.check_prefill(p, label=case)
+
+
+def test_scale_and_aliased_state():
+    p = inputs.make("prefill", seed=8, B=2, T=150, H=3, s0=True)
+    U.check_prefill(p, label="alias+scale", alias_state=True,
+                    scale=0.0883883)
+
+
+def test_zero_length_keeps_state():
+    p = inputs.make("prefill", seed=2, B=2, T=0, H=2, s0=True)
+    o, s = U.run_prefill_gpu(p)
+    assert o.shape == (2, 0, 2, 128)
+    assert np.array_equal(s, p.initial_state.astype(np.float64))
+
+
+def test_varlen_ragged_with_states():
+    p = inputs.make("varlen", seed=3, H=3, lengths=[0, 1, 63, 64, 65, 200, 0,
+                                                     129])
+    U.check_prefill(p, label="varlen ragged")
+    U.check_prefill(p, label="varlen aliased", alias_state=True)
+
+
+def test_varlen_without_initial_state():
+    p = inputs.make("varlen", seed=4, H=2, s0=False,
+                    lengths=[100, 37, 256])
+    U.check_prefill(p, label="varlen zero state")
+
+
+def test_split_resume_on_gpu():
+    """Prefill of T tokens == prefill of T1 tokens, then append-prefill of
+    the rest from the returned state."""
+    p = inputs.make("prefill", seed=6, B=1, T=400, H=2, s0=True)
+    o_all, s_all = U.run_prefill_gpu(p)
+    T1 = 137
+    dev = lambda x: U.to_dev(x, p.dtype)  # noqa: E731
+    o1, s1 = kda.kda_prefill_chunked(dev(p.q[:, :T1]), dev(p.k[:, :T1]),
+                                     dev(p.v[:, :T1]), U.f32_dev(p.g[:, :T1]),
+                                     U.f32_dev(p.beta[:, :T1]),
+                                     U.f32_dev(p.initial_state))
+    o2, s2 = kda.kda_prefill_chunked(dev(p.q[:, T1:]), dev(p.k[:, T1:]),
+                                     dev(p.v[:, T1:]), U.f32_dev(p.g[:, T1:]),
+                                     U.f32_dev(p.beta[:, T1:]), s1)
+    torch.cuda.synchronize()
+    o_split = np.concatenate([U.host(o1), U.host(o2)], axis=1)
+    o_ref, s_ref = U.run_oracle(p)
+    assert U.slice_rel(o_split, o_ref, (0, 2)) < 2e-2
+    assert U.slice_rel(U.host(s2), s_ref, (0, 1)) < 2e-2
+    assert U.slice_rel(o_split, o_all, (0, 2)) < 2e-2
+
+
+def test_prefill_deterministic():
+    p = inputs.make("prefill", seed=7, B=1, T=500, H=4, s0=True)
+    a = U.run_prefill_gpu(p)
+    b = U.run_prefill_gpu(p)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---- full-size workloads, sampled heads -----------------------------------
+def test_full_prefill_workload_sampled_heads():
+    """H=96, T=8192, d=128, C=64, bf16, zero state."""
+    p = inputs.make("prefill", seed=0)
+    U.check_prefill(p, heads=[0, 41, 95], label="prefill full")
+
+
+def test_full_long_context_sampled_head():
+    """H=32, T=131072, d=128, C=64, bf16, nonzero state, decay near -5."""
+    p = inputs.make("long", seed=0)
+    U.check_prefill(p, heads=[17], label="long full")
+
+
+def test_full_varlen_append_sampled_heads():
+    """8 sequences of 1024..16384 tokens, H=96, each from a cached state."""
+    p = inputs.make("varlen", seed=0)
+    U.log("varlen lengths", p.seq_lengths.tolist())
+    U.check_prefill(p, heads=[5, 90], label="varlen full")
