@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one pass of the whole path over resident synthetic inputs:
+  * chunked prefill of 1 x 8192 tokens, 96 heads, d_k = d_v = 128, C = 64,
+    bf16 q/k/v, fp32 g/beta, zero initial state -> outputs + final state
+    (chunk-prep kernel, then chunk-recurrence kernel), and
+  * one decode step of 64 sequences x 96 heads, d = 128, fp32 state
+    ~N(0, 0.02^2) updated in place, bf16 q/k/v (decode kernel).
+
+Prints ONE JSON line.  `value` is the decode step's state throughput in GB/s
+(8 * d^2 bytes per head and token, the fp32 state read and written once:
+"Kimi K3: The Manos, The Mythos, The Legendos", section "Complexity
+analysis"); the prefill's tokens/s, FLOP and byte rates ride in the same
+line.  Kernel durations come from HIP events on the stream the kernels run
+on.  Decode rotates three state buffers so that consecutive steps never
+find the state in the 256 MB Infinity Cache.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from linear_recurrent_attention_kda_amd import counts, inputs  # noqa: E402
+
+METRIC = ("KDA prefill tokens/s + decode state GB/s (H=96,D=128) on 1 MI355X, "
+          "% roofline")
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "linear_recurrent_attention_kda_amd", "csrc")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_hash(name: str) -> str:
+    h = hashlib.sha256()
+    for f in (name, "kda_device.hpp", "kda_internal.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_file: str):
+    """HBM bytes per launch measured with rocprofv3 counters for the current
+    source of `kernel_file` (profiles/traffic_<name>.txt), or None when no
+    measurement exists or the kernel changed since it was taken."""
+    path = os.path.join(PROFILES, "traffic_%s.txt" %
+                        kernel_file.replace(".hip", ""))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("source_sha256_16") != source_hash(kernel_file):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--prefill", default="prefill",
+                    choices=["prefill", "long", "varlen"],
+                    help="prefill workload timed in each step")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the oracle on the host cores")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB per "
+                         "step (reference kernel for HBM counter scaling)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; KDA shards over "
+              "(sequence, head) with no communication, so a multi-GPU run "
+              "is one independent copy per GPU (see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    from linear_recurrent_attention_kda_amd import kda
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kda.load()  # fails loudly if libkda.so is missing
+
+    # ---------------- inputs (seeded, resident in HBM before timing) -------
+    t_gen = time.time()
+    dp = inputs.make("decode", seed=0)
+    pp = inputs.make(args.prefill, seed=0)
+    log("inputs generated in %.1fs" % (time.time() - t_gen))
+
+    def to_dev(x, dt):
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        return (t.to(torch.bfloat16) if dt == "bf16" else t).to(dev)
+
+    dq, dk, dv = (to_dev(x, dp.dtype) for x in (dp.q, dp.k, dp.v))
+    dg, dbeta = to_dev(dp.g, "fp32"), to_dev(dp.beta, "fp32")
+    states = [to_dev(dp.initial_state, "fp32") for _ in range(3)]
+    do = torch.empty((dp.B, dp.H, dp.V), dtype=dq.dtype, device=dev)
+
+    pq, pk, pv = (to_dev(x, pp.dtype) for x in (pp.q, pp.k, pp.v))
+    pg, pbeta = to_dev(pp.g, "fp32"), to_dev(pp.beta, "fp32")
+    ps0 = None if pp.initial_state is None else to_dev(pp.initial_state,
+                                                       "fp32")
+    if pp.kind == "varlen":
+        cu = torch.from_numpy(pp.cu_seqlens).to(dev)
+        nseq, total = len(pp.cu_seqlens) - 1, int(pp.cu_seqlens[-1])
+        maxlen = int(pp.seq_lengths.max())
+        po = torch.empty((total, pp.H, pp.V), dtype=pq.dtype, device=dev)
+    else:
+        nseq, total = pp.B, pp.B * pp.T
+        po = torch.empty((pp.B, pp.T, pp.H, pp.V), dtype=pq.dtype, device=dev)
+    pfs = torch.empty((nseq, pp.H, pp.K, pp.V), dtype=torch.float32,
+                      device=dev)
+    ws = kda.workspace_for(nseq, total, pp.H, pp.K, pp.V, pp.C, dev)
+    calib = None
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        calib = (torch.ones(n, dtype=torch.float32, device=dev),
+                 torch.empty(n, dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def prefill():
+        if pp.kind == "varlen":
+            kda.kda_prefill_varlen(pq, pk, pv, pg, pbeta, cu, maxlen, ps0,
+                                   chunk_size=pp.C, final_state=pfs, o=po,
+                                   workspace=ws)
+        else:
+            kda.kda_prefill_chunked(pq, pk, pv, pg, pbeta, ps0,
+                                    chunk_size=pp.C, final_state=pfs, o=po,
+                                    workspace=ws)
+
+    def decode(i):
+        kda.kda_decode_step(dq, dk, dv, dg, dbeta, states[i % 3], o=do)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(i, rec=None):
+        if rec is not None:
+            e0, e1, e2 = ev(), ev(), ev()
+            e0.record(stream)
+        prefill()
+        if rec is not None:
+            e1.record(stream)
+        decode(i)
+        if rec is not None:
+            e2.record(stream)
+            rec.append((e0, e1, e2))
+        if calib is not None:
+            calib[1].copy_(calib[0])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log("warmup done (%d steps)" % args.warmup)
+
+    rec = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [a.elapsed_time(b) for a, b, _ in rec]
+    dec_ms = [b.elapsed_time(c) for _, b, c in rec]
+    ms_step = wall * 1e3 / args.steps
+    pre_avg = float(np.mean(pre_ms))
+    dec_avg = float(np.mean(dec_ms))
+    log("timed %d steps: %.3f ms/step, prefill %.3f ms, decode %.4f ms"
+        % (args.steps, ms_step, pre_avg, dec_avg))
+
+    # ---------------- derived figures --------------------------------------
+    D, H = dp.K, dp.H
+    dec_bytes = counts.decode_bytes_per_head(D) * dp.B * H
+    dec_gbps = dec_bytes / (dec_avg * 1e-3) / 1e9
+    chunks = int(np.sum((pp.seq_lengths + pp.C - 1) // pp.C)) * pp.H
+    pre_flops = counts.prefill_flops_per_chunk(pp.C, D) * chunks
+    pre_bytes_pages = (counts.prefill_bytes_per_chunk(pp.C, D) * chunks +
+                       counts.decode_bytes_per_head(D) * nseq * pp.H)
+    pre_bytes_min = (counts.prefill_min_bytes_per_token_head(pp.K, pp.V) *
+                     total * pp.H)
+    pre_s = pre_avg * 1e-3
+    traffic = read_traffic("kda_decode.hip")
+
+    result = {
+        "metric": METRIC,
+        "value": round(dec_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), "
+                "g=-5*sigmoid(N(0,1)), beta=sigmoid(N(0,1)), "
+                "state N(0,0.02^2))",
+        "config": {
+            "workload": "KDA decode step: B=64 sequences, H=96, "
+                        "d_k=d_v=128, fp32 state in place, bf16 q/k/v; "
+                        "each step also runs the chunked prefill below",
+            "decode_batch": dp.B, "heads": H, "head_dim": D,
+            "prefill_workload": "%s: %d sequence(s), %d tokens, H=%d, d=%d, "
+                                "C=%d, %s q/k/v, %s initial state"
+                                % (pp.name, nseq, total, pp.H, pp.K, pp.C,
+                                   pp.dtype, "zero" if ps0 is None
+                                   else "nonzero"),
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "decode_kernel (kda_decode.hip)",
+            "bound": "hbm",
+            "achieved": round(dec_gbps, 2),
+            "peak": counts.HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(dec_gbps / counts.HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dec_bytes,
+            "avg_launch_ms": round(dec_avg, 5),
+        },
+        "prefill": {
+            "tokens_per_s": round(total / pre_s, 1),
+            "ms": round(pre_avg, 4),
+            "unit": "tokens/s",
+            "pages_flops": pre_flops,
+            "tflops": round(pre_flops / pre_s / 1e12, 2),
+            "mfma_util_frac": round(pre_flops / pre_s / 1e12 /
+                                    counts.BF16_MFMA_PEAK_TFLOPS, 4),
+            "roofline": {
+                "kernels": "prep_kernel + recur_kernel (one library call)",
+                "bound": "hbm",
+                "achieved": round(pre_bytes_pages / pre_s / 1e9, 2),
+                "peak": counts.HBM_PEAK_GBPS,
+                "unit": "GB/s",
+                "frac": round(pre_bytes_pages / pre_s / 1e9 /
+                              counts.HBM_PEAK_GBPS, 4),
+                "algorithmic_bytes": pre_bytes_pages,
+                "minimal_bytes": pre_bytes_min,
+                "minimal_bytes_frac": round(pre_bytes_min / pre_s / 1e9 /
+                                            counts.HBM_PEAK_GBPS, 4),
+            },
+        },
+    }
+
+    # ---------------- CPU baseline: the oracle on the host cores -----------
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(dp, pp)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline(dp, pp):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same
+    workloads: the whole decode step, and one prefill head per thread over
+    all of the prefill's tokens (scaled to all heads)."""
+    import oracle
+    oracle.build(force=False)
+    threads = min(16, os.cpu_count() or 1)
+    oracle.set_threads(threads)
+    t = time.perf_counter()
+    oracle.run_decode(dp.q, dp.k, dp.v, dp.g, dp.beta, dp.initial_state)
+    dec_s = time.perf_counter() - t
+    dec_bytes = counts.decode_bytes_per_head(dp.K) * dp.B * dp.H
+    heads = list(range(min(threads, pp.H)))
+    sel = lambda x: x[..., heads, :]  # noqa: E731
+    t = time.perf_counter()
+    if pp.kind == "varlen":
+        oracle.run_varlen(sel(pp.q), sel(pp.k), sel(pp.v), sel(pp.g),
+                          pp.beta[..., heads], pp.cu_seqlens,
+                          None if pp.initial_state is None
+                          else pp.initial_state[:, heads])
+        total = int(pp.cu_seqlens[-1])
+    else:
+        oracle.run_fixed(sel(pp.q), sel(pp.k), sel(pp.v), sel(pp.g),
+                         pp.beta[..., heads],
+                         None if pp.initial_state is None
+                         else pp.initial_state[:, heads])
+        total = pp.B * pp.T
+    pre_s = time.perf_counter() - t
+    pre_tps = total / (pre_s * pp.H / len(heads))
+    log("oracle: decode %.2fs, prefill sample %.2fs" % (dec_s, pre_s))
+    return {
+        "value": round(dec_bytes / dec_s / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "whole decode step (64x96 heads, d=128) in fp64; prefill: "
+                  "%d of %d heads over all %d tokens, scaled to all heads"
+                  % (len(heads), pp.H, total),
+        "prefill_tokens_per_s": round(pre_tps, 1),
+        "decode_seconds": round(dec_s, 3),
+        "prefill_sample_seconds": round(pre_s, 3),
+        "cpu_model": cpu_model(),
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

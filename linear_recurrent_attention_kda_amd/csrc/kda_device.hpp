@@ -42,6 +42,37 @@ __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
+// Eight consecutive storage-dtype elements kept raw in registers (a
+// prefetch buffer), converted to float on use.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const bf16* p) {
+    v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+  }
+  __device__ __forceinline__ void zero() {
+    v = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
+  }
+  __device__ __forceinline__ void get(float (&x)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
+  }
+};
+template <> struct Raw8<float> {
+  float4 lo, hi;
+  __device__ __forceinline__ void load(const float* p) {
+    lo = *reinterpret_cast<const float4*>(p);
+    hi = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() {
+    lo = hi = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __device__ __forceinline__ void get(float (&x)[8]) const {
+    x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w;
+    x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
+  }
+};
+
 __device__ __forceinline__ bf16x8 pack8(const float (&x)[8]) {
   bf16x8 r;
 #pragma unroll

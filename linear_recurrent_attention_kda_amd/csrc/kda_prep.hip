@@ -36,283 +36,387 @@
 namespace kda {
 namespace {
 
+// Work item = (sequence n, chunk ci, head h), heads fastest so that the
+// workgroups running together read whole contiguous token rows.
+struct Item {
+  int n, ci, h;
+  int64_t t0;
+  int L;
+  bool valid;
+};
+
+__device__ __forceinline__ Item decode_item(const PrefillArgs& a, int C,
+                                            int64_t item) {
+  Item it;
+  it.h = (int)(item % a.H);
+  const int64_t rest = item / a.H;
+  it.ci = (int)(rest % a.max_chunks);
+  it.n = (int)(rest / a.max_chunks);
+  int64_t bos, eos;
+  seq_bounds(a, it.n, bos, eos);
+  it.t0 = bos + (int64_t)it.ci * C;
+  it.valid = it.t0 < eos;
+  it.L = it.valid ? ((eos - it.t0) < C ? (int)(eos - it.t0) : C) : 0;
+  return it;
+}
+
 template <typename Tin, int D, int C>
-__global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a,
+                                                   int64_t total_items) {
   constexpr int K = D, V = D;
   constexpr int NSUB = C / 16;             // 16-row sub-tiles per chunk
-  constexpr int KSTEPS = (K + 31) / 32;    // 32-deep MFMA steps over K
+  constexpr int KSTEPS = (K + 31) / 32;    // 32-wide column groups of a row
   constexpr int TPC = 256 / K;             // scan threads per channel
   constexpr int RPT = C / TPC;             // rows per scan thread
   constexpr int AP = K + 4;                // padded strides (bank spread)
   constexpr int CP = C + 4;
   constexpr int TP = C + 8;
+  constexpr int KP = K + 8;
   static_assert(NSUB >= 1 && NSUB <= 4 && C % TPC == 0 && K <= 256, "shape");
+  constexpr int ABUF = C * (AP > CP ? AP : CP);
 
-  __shared__ float s_a[C][AP];             // cumulative log2-decay
+  // s_a (cumulative log2-decay) is dead once A and M are formed; the
+  // inverse then reuses its storage.
+  __shared__ __attribute__((aligned(16))) float s_abuf[ABUF];
+  float (*s_a)[AP] = reinterpret_cast<float (*)[AP]>(s_abuf);
+  float (*s_inv)[CP] = reinterpret_cast<float (*)[CP]>(s_abuf);
   __shared__ float s_A[C][CP];             // beta-scaled strictly-lower A
-  __shared__ float s_inv[C][CP];           // (I + A)^-1
+  __shared__ __attribute__((aligned(16))) Tin s_k[C][KP];     // k rows
   __shared__ __attribute__((aligned(16))) bf16 s_kbT[K][TP];  // (beta k e^a)^T
   __shared__ __attribute__((aligned(16))) bf16 s_vbT[V][TP];  // (beta v)^T
   __shared__ float s_tmp[4][16][20];
   __shared__ float s_beta[C];
   __shared__ float s_tot[TPC][K];
 
-  const int n = blockIdx.z, h = blockIdx.y, ci = blockIdx.x;
-  int64_t bos, eos;
-  seq_bounds(a, n, bos, eos);
-  const int64_t t0 = bos + (int64_t)ci * C;
-  if (t0 >= eos) return;
-  const int L = (eos - t0) < C ? (int)(eos - t0) : C;
-  const int64_t slot = t0 / C + n;
   const int H = a.H;
-
-  const WsLayout lay = WsLayout::make(C, K, V);
-  char* blk = a.ws + ((size_t)h * a.nslots + slot) * lay.block_bytes;
-  bf16* gW = reinterpret_cast<bf16*>(blk + lay.off_W);
-  bf16* gQh = reinterpret_cast<bf16*>(blk + lay.off_Qh);
-  bf16* gKbT = reinterpret_cast<bf16*>(blk + lay.off_KbT);
-  bf16* gUtT = reinterpret_cast<bf16*>(blk + lay.off_UtT);
-  bf16* gM = reinterpret_cast<bf16*>(blk + lay.off_M);
-  float* gGamma = reinterpret_cast<float*>(blk + lay.off_gamma);
-
-  const Tin* q = static_cast<const Tin*>(a.q);
-  const Tin* k = static_cast<const Tin*>(a.k);
-  const Tin* v = static_cast<const Tin*>(a.v);
-  auto qrow = [&](int r) { return q + ((t0 + r) * H + h) * (int64_t)K; };
-  auto krow = [&](int r) { return k + ((t0 + r) * H + h) * (int64_t)K; };
-  auto vrow = [&](int r) { return v + ((t0 + r) * H + h) * (int64_t)V; };
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rl = lane & 15, kg = lane >> 4;
+  const int sc = tid % K, sseg = tid / K;  // scan layout
+  const int rrow = 16 * wave + rl;         // row-operand layout row
+  const bool has_row = wave < NSUB;
+  const Tin* qg = static_cast<const Tin*>(a.q);
+  const Tin* kgp = static_cast<const Tin*>(a.k);
+  const Tin* vg = static_cast<const Tin*>(a.v);
+  const WsLayout lay = WsLayout::make(C, K, V);
 
-  // ---- 1. cumulative decay a (log2 units) per channel --------------------
-  {
-    const int c = tid % K, seg = tid / K;
-    float loc[RPT];
-    float run = 0.f;
+  // Prefetch registers (one item ahead).  g in the scan layout; q, k, v in
+  // the row-operand layout (row 16*wave + lane%16, columns 32ks + 8kg).
+  float rg[RPT];
+  Raw8<Tin> rq[KSTEPS], rk[KSTEPS], rv[KSTEPS];
+  float rbeta = 0.f;
+
+  auto load_gvb = [&](const Item& it) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int r = seg * RPT + i;
-      const float gv =
-          r < L ? a.g[((t0 + r) * H + h) * (int64_t)K + c] : 0.f;
-      run += gv * kLog2e;
-      loc[i] = run;
+      const int r = sseg * RPT + i;
+      rg[i] = r < it.L ? a.g[((it.t0 + r) * H + it.h) * (int64_t)K + sc] : 0.f;
     }
-    s_tot[seg][c] = run;
-    if (tid < C) s_beta[tid] = tid < L ? a.beta[(t0 + tid) * H + h] : 0.f;
-    for (int i = tid; i < C * CP; i += 256) (&s_inv[0][0])[i] = 0.f;
-    __syncthreads();
-    float off = 0.f;
-    for (int j = 0; j < seg; ++j) off += s_tot[j][c];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) s_a[seg * RPT + i][c] = loc[i] + off;
-    if (seg == TPC - 1)
-      gGamma[c] = __builtin_amdgcn_exp2f(loc[RPT - 1] + off);
-  }
-  __syncthreads();
-
-  // ---- 2. elementwise: Q^ (global), K-bar^T (global), (beta k e^a)^T and
-  //         (beta v)^T (LDS) ------------------------------------------------
-  for (int it = tid; it < C * (K / 8); it += 256) {
-    const int r = it / (K / 8), c0 = 8 * (it % (K / 8));
-    float x[8];
-    if (r < L) {
-      load8(qrow(r) + c0, x);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] *= __builtin_amdgcn_exp2f(s_a[r][c0 + i]);
-    *reinterpret_cast<bf16x8*>(gQh + r * K + c0) = pack8(x);
-  }
-  for (int it = tid; it < K * (C / 8); it += 256) {
-    const int c = it % K, s0 = 8 * (it / K);
-    const float alast = s_a[C - 1][c];
-    float kb[8], kh[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int s = s0 + i;
-      const float kv = s < L ? io<Tin>::to_f(krow(s)[c]) : 0.f;
-      kb[i] = kv * __builtin_amdgcn_exp2f(alast - s_a[s][c]);
-      kh[i] = s_beta[s] * kv * __builtin_amdgcn_exp2f(s_a[s][c]);
-    }
-    *reinterpret_cast<bf16x8*>(gKbT + c * C + s0) = pack8(kb);
-    *reinterpret_cast<bf16x8*>(&s_kbT[c][s0]) = pack8(kh);
-  }
-  for (int it = tid; it < V * (C / 8); it += 256) {
-    const int j = it % V, s0 = 8 * (it / V);
-    float vb[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int s = s0 + i;
-      vb[i] = s < L ? s_beta[s] * io<Tin>::to_f(vrow(s)[j]) : 0.f;
-    }
-    *reinterpret_cast<bf16x8*>(&s_vbT[j][s0]) = pack8(vb);
-  }
-
-  // ---- 3. A (LDS, fp32) and M (global, bf16) per 16-row sub-tile ---------
-  if (wave < NSUB) {
-    const int m = wave;
-    const int rl = lane & 15, cb = 8 * (lane >> 4);
-    const int r = 16 * m + rl;
-    bf16x8 kr[KSTEPS], qr[KSTEPS];
+    const bool row = has_row && rrow < it.L;
+    rbeta = row ? a.beta[(it.t0 + rrow) * H + it.h] : 0.f;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int c0 = 32 * ks + cb;
-      float kx[8], qx[8];
-      if (c0 < K && r < L) {
-        load8(krow(r) + c0, kx);
-        load8(qrow(r) + c0, qx);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) kx[i] = qx[i] = 0.f;
-      }
-      if (c0 < K) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float rho = m > 0 ? s_a[16 * m - 1][c0 + i] : 0.f;
-          const float f = __builtin_amdgcn_exp2f(s_a[r][c0 + i] - rho);
-          kx[i] *= f;
-          qx[i] *= f;
-        }
-      }
-      kr[ks] = pack8(kx);
-      qr[ks] = pack8(qx);
+      const int c0 = 32 * ks + 8 * kg;
+      if (row && c0 < V)
+        rv[ks].load(vg + ((it.t0 + rrow) * H + it.h) * (int64_t)V + c0);
+      else
+        rv[ks].zero();
     }
-    for (int nn = 0; nn < NSUB; ++nn) {
-      if (nn > m) {
-        // M is zero above the diagonal sub-tile.
-        *reinterpret_cast<uint2*>(gM + r * C + 16 * nn + 4 * (lane >> 4)) =
-            make_uint2(0u, 0u);
-        continue;
+  };
+  auto load_qk = [&](const Item& it) {
+    const bool row = has_row && rrow < it.L;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int c0 = 32 * ks + 8 * kg;
+      if (row && c0 < K) {
+        const int64_t base = ((it.t0 + rrow) * H + it.h) * (int64_t)K + c0;
+        rq[ks].load(qg + base);
+        rk[ks].load(kgp + base);
+      } else {
+        rq[ks].zero();
+        rk[ks].zero();
       }
-      const int s = 16 * nn + rl;
-      f32x4 accA = zero4(), accMT = zero4();
+    }
+  };
+
+  int64_t item = blockIdx.x;
+  int64_t have = -1;  // item whose inputs the prefetch registers hold
+  if (item < total_items) {
+    const Item it = decode_item(a, C, item);
+    if (it.valid) {
+      load_gvb(it);
+      load_qk(it);
+      have = item;
+    }
+  }
+
+  for (; item < total_items; item += gridDim.x) {
+    const Item it = decode_item(a, C, item);
+    if (!it.valid) continue;  // uniform across the workgroup
+    if (have != item) {
+      load_gvb(it);
+      load_qk(it);
+    }
+    const int64_t next = item + gridDim.x;
+    Item nx;
+    nx.valid = false;
+    if (next < total_items) nx = decode_item(a, C, next);
+    const int L = it.L;
+    const int h = it.h;
+    const int64_t slot = it.t0 / C + it.n;
+    char* blk = a.ws + ((size_t)h * a.nslots + slot) * lay.block_bytes;
+    bf16* gW = reinterpret_cast<bf16*>(blk + lay.off_W);
+    bf16* gQh = reinterpret_cast<bf16*>(blk + lay.off_Qh);
+    bf16* gKbT = reinterpret_cast<bf16*>(blk + lay.off_KbT);
+    bf16* gUtT = reinterpret_cast<bf16*>(blk + lay.off_UtT);
+    bf16* gM = reinterpret_cast<bf16*>(blk + lay.off_M);
+    float* gGamma = reinterpret_cast<float*>(blk + lay.off_gamma);
+
+    __syncthreads();  // the previous item is done with every LDS buffer
+
+    // ---- 1. stage: decay scan, beta, k rows, (beta v)^T ------------------
+    float loc[RPT];
+    {
+      float run = 0.f;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        run += rg[i] * kLog2e;
+        loc[i] = run;
+      }
+      s_tot[sseg][sc] = run;
+    }
+    if (has_row) {
+      s_beta[rrow] = rbeta;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int c0 = 32 * ks + cb;
-        float kx[8];
-        if (c0 < K && s < L) {
-          load8(krow(s) + c0, kx);
+        const int c0 = 32 * ks + 8 * kg;
+        if (c0 < K) {
+          *reinterpret_cast<Raw8<Tin>*>(&s_k[rrow][c0]) = rk[ks];
+        }
+        if (c0 < V) {
+          float x[8];
+          rv[ks].get(x);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s_vbT[c0 + i][rrow] = (bf16)(rbeta * x[i]);
+        }
+      }
+    }
+    __syncthreads();
+    {
+      float off = 0.f;
+      for (int j = 0; j < sseg; ++j) off += s_tot[j][sc];
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) s_a[sseg * RPT + i][sc] = loc[i] + off;
+      if (sseg == TPC - 1)
+        gGamma[sc] = __builtin_amdgcn_exp2f(loc[RPT - 1] + off);
+    }
+    if (nx.valid) load_gvb(nx);  // g, v, beta registers are free now
+    __syncthreads();
+
+    // ---- 2. Q^ (from registers), K-bar^T (global) and (beta k e^a)^T -----
+    if (has_row) {
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int c0 = 32 * ks + 8 * kg;
+        if (c0 < K) {
+          float x[8];
+          rq[ks].get(x);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            x[i] *= __builtin_amdgcn_exp2f(s_a[rrow][c0 + i]);
+          *reinterpret_cast<bf16x8*>(gQh + rrow * K + c0) = pack8(x);
+        }
+      }
+    }
+    for (int e = tid; e < K * (C / 8); e += 256) {
+      const int c = e % K, s0 = 8 * (e / K);
+      const float alast = s_a[C - 1][c];
+      float kb[8], kh[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int s = s0 + i;
+        const float kv = io<Tin>::to_f(s_k[s][c]);
+        const float as = s_a[s][c];
+        kb[i] = kv * __builtin_amdgcn_exp2f(alast - as);
+        kh[i] = s_beta[s] * kv * __builtin_amdgcn_exp2f(as);
+      }
+      *reinterpret_cast<bf16x8*>(gKbT + c * C + s0) = pack8(kb);
+      *reinterpret_cast<bf16x8*>(&s_kbT[c][s0]) = pack8(kh);
+    }
+
+    // ---- 3. A (LDS, fp32) and M (global, bf16) per 16-row sub-tile -------
+    if (has_row) {
+      const int m = wave;
+      bf16x8 kr[KSTEPS], qr[KSTEPS];
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int c0 = 32 * ks + 8 * kg;
+        float kx[8], qx[8];
+        rk[ks].get(kx);
+        rq[ks].get(qx);
+        if (c0 < K) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const float rho = m > 0 ? s_a[16 * m - 1][c0 + i] : 0.f;
-            kx[i] *= __builtin_amdgcn_exp2f(rho - s_a[s][c0 + i]);
+            const float f = __builtin_amdgcn_exp2f(s_a[rrow][c0 + i] - rho);
+            kx[i] *= f;
+            qx[i] *= f;
           }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) kx[i] = 0.f;
         }
-        const bf16x8 kc = pack8(kx);
-        accA = mfma_bf16(kr[ks], kc, accA);    // A tile: rows r, cols s
-        accMT = mfma_bf16(kc, qr[ks], accMT);  // M^T tile: rows s, cols r
+        kr[ks] = pack8(kx);
+        qr[ks] = pack8(qx);
       }
-      // A tile in D layout: row 16m + 4(lane/16) + i, column 16nn + lane%16.
+      for (int nn = 0; nn < NSUB; ++nn) {
+        if (nn > m) {
+          // M is zero above the diagonal sub-tile.
+          *reinterpret_cast<uint2*>(gM + rrow * C + 16 * nn + 4 * kg) =
+              make_uint2(0u, 0u);
+          continue;
+        }
+        const int s = 16 * nn + rl;
+        f32x4 accA = zero4(), accMT = zero4();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = 16 * m + 4 * (lane >> 4) + i, ss = 16 * nn + rl;
-        s_A[rr][ss] = ss < rr ? s_beta[rr] * accA[i] : 0.f;
-      }
-      // M^T tile: row (of M^T) s = 16nn + 4(lane/16) + i, column r.
-      bf16x4 mv;
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          const int c0 = 32 * ks + 8 * kg;
+          float kx[8];
+          if (c0 < K) {
+            const Raw8<Tin> raw = *reinterpret_cast<const Raw8<Tin>*>(&s_k[s][c0]);
+            raw.get(kx);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ss = 16 * nn + 4 * (lane >> 4) + i;
-        mv[i] = (bf16)(ss <= r ? accMT[i] : 0.f);
+            for (int i = 0; i < 8; ++i) {
+              const float rho = m > 0 ? s_a[16 * m - 1][c0 + i] : 0.f;
+              kx[i] *= __builtin_amdgcn_exp2f(rho - s_a[s][c0 + i]);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) kx[i] = 0.f;
+          }
+          const bf16x8 kc = pack8(kx);
+          accA = mfma_bf16(kr[ks], kc, accA);    // A tile: rows r, cols s
+          accMT = mfma_bf16(kc, qr[ks], accMT);  // M^T tile: rows s, cols r
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 16 * m + 4 * kg + i, ss = 16 * nn + rl;
+          s_A[rr][ss] = ss < rr ? s_beta[rr] * accA[i] : 0.f;
+        }
+        bf16x4 mv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ss = 16 * nn + 4 * kg + i;
+          mv[i] = (bf16)(ss <= rrow ? accMT[i] : 0.f);
+        }
+        *reinterpret_cast<bf16x4*>(gM + rrow * C + 16 * nn + 4 * kg) = mv;
       }
-      *reinterpret_cast<bf16x4*>(gM + r * C + 16 * nn + 4 * (lane >> 4)) = mv;
     }
-  }
-  __syncthreads();
+    if (nx.valid) {
+      load_qk(nx);  // q, k registers are free now
+      have = next;
+    } else {
+      have = -1;
+    }
+    __syncthreads();  // A complete; decay buffer no longer read
 
-  // ---- 4. INV = (I + A)^-1: diagonal 16x16 blocks by forward substitution
-  //         (one column per lane), then off-diagonal blocks by levels:
-  //         INV_mn = -INV_mm * sum_{j=n}^{m-1} A_mj INV_jn --------------------
-  if (wave < NSUB && lane < 16) {
-    const int m = wave, j = lane, b = 16 * m;
-    float x[16];
+    // ---- 4. INV = (I + A)^-1: diagonal 16x16 blocks by forward
+    //         substitution (one column per lane), then off-diagonal blocks by
+    //         levels: INV_mn = -INV_mm * sum_{j=n}^{m-1} A_mj INV_jn ---------
+    for (int i = tid; i < C * CP; i += 256) (&s_inv[0][0])[i] = 0.f;
+    __syncthreads();
+    if (has_row && lane < 16) {
+      const int m = wave, j = lane, b = 16 * m;
+      float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = (r == j) ? 1.f : 0.f;
+      for (int r = 0; r < 16; ++r) {
+        float acc = (r == j) ? 1.f : 0.f;
 #pragma unroll
-      for (int s = 0; s < r; ++s) acc -= s_A[b + r][b + s] * x[s];
-      x[r] = acc;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s_inv[b + r][b + j] = x[r];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int d = 1; d < NSUB; ++d) {
-    const int nb = wave, mb = wave + d;
-    if (mb < NSUB) {
-      const int rl = lane & 15, kg = lane >> 4;
-      f32x4 t = zero4();
-      for (int j = nb; j < mb; ++j) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          t = mfma_f32(s_A[16 * mb + rl][16 * j + 4 * kk + kg],
-                       s_inv[16 * j + 4 * kk + kg][16 * nb + rl], t);
+        for (int s2 = 0; s2 < r; ++s2) acc -= s_A[b + r][b + s2] * x[s2];
+        x[r] = acc;
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_tmp[wave][4 * kg + i][rl] = t[i];
-      f32x4 u = zero4();
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        u = mfma_f32(s_inv[16 * mb + rl][16 * mb + 4 * kk + kg],
-                     s_tmp[wave][4 * kk + kg][rl], u);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s_inv[16 * mb + 4 * kg + i][16 * nb + rl] = -u[i];
+      for (int r = 0; r < 16; ++r) s_inv[b + r][b + j] = x[r];
     }
     __syncthreads();
-  }
-
-  // ---- 5. W = INV (beta k e^a) (stored row-major via W^T tiles) and
-  //         U~ = INV (beta v) (stored transposed) --------------------------
-  {
-    constexpr int KT = K / 16, VT = V / 16;
-    constexpr int NT = NSUB * (KT + VT);
-    const int rl = lane & 15, kg = lane >> 4;
-    for (int t = wave; t < NT; t += 4) {
-      const int m = t / (KT + VT), ct = t % (KT + VT);
-      const bool isW = ct < KT;
-      const int col = 16 * (isW ? ct : ct - KT) + rl;
-      const int r = 16 * m + rl;
-      const int csteps = (16 * (m + 1) + 31) / 32;
-      f32x4 acc = zero4();
-      for (int cs = 0; cs < csteps; ++cs) {
-        const int s0 = 32 * cs + 8 * kg;
-        bf16x8 iv = zero_bf16x8(), bv = zero_bf16x8();
-        if (s0 < C) {
-          float x[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) x[i] = s_inv[r][s0 + i];
-          iv = pack8(x);
-          bv = *reinterpret_cast<const bf16x8*>(isW ? &s_kbT[col][s0]
-                                                    : &s_vbT[col][s0]);
+    for (int d = 1; d < NSUB; ++d) {
+      const int nb = wave, mb = wave + d;
+      if (mb < NSUB) {
+        f32x4 t = zero4();
+        for (int j = nb; j < mb; ++j) {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            t = mfma_f32(s_A[16 * mb + rl][16 * j + 4 * kk + kg],
+                         s_inv[16 * j + 4 * kk + kg][16 * nb + rl], t);
         }
-        acc = isW ? mfma_bf16(bv, iv, acc)   // W^T tile: rows c, cols r
-                  : mfma_bf16(iv, bv, acc);  // U~ tile: rows r, cols j
-      }
-      bf16x4 ov;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ov[i] = (bf16)acc[i];
-      if (isW) {
-        // W[r = 16m + lane%16][c = 16ct + 4(lane/16) + i]
-        *reinterpret_cast<bf16x4*>(gW + r * K + 16 * ct + 4 * kg) = ov;
-      } else {
-        // U~^T[j = col][r = 16m + 4(lane/16) + i]
-        *reinterpret_cast<bf16x4*>(gUtT + col * C + 16 * m + 4 * kg) = ov;
+        for (int i = 0; i < 4; ++i) s_tmp[wave][4 * kg + i][rl] = t[i];
+        f32x4 u = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          u = mfma_f32(s_inv[16 * mb + rl][16 * mb + 4 * kk + kg],
+                       s_tmp[wave][4 * kk + kg][rl], u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s_inv[16 * mb + 4 * kg + i][16 * nb + rl] = -u[i];
+      }
+      __syncthreads();
+    }
+
+    // ---- 5. W = INV (beta k e^a) (row-major, via W^T tiles) and
+    //         U~ = INV (beta v) (stored transposed) ------------------------
+    {
+      constexpr int KT = K / 16, VT = V / 16;
+      constexpr int NT = NSUB * (KT + VT);
+      for (int t = wave; t < NT; t += 4) {
+        const int m = t / (KT + VT), ct = t % (KT + VT);
+        const bool isW = ct < KT;
+        const int col = 16 * (isW ? ct : ct - KT) + rl;
+        const int r = 16 * m + rl;
+        const int csteps = (16 * (m + 1) + 31) / 32;
+        f32x4 acc = zero4();
+        for (int cs = 0; cs < csteps; ++cs) {
+          const int s0 = 32 * cs + 8 * kg;
+          bf16x8 iv = zero_bf16x8(), bv = zero_bf16x8();
+          if (s0 < C) {
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = s_inv[r][s0 + i];
+            iv = pack8(x);
+            bv = *reinterpret_cast<const bf16x8*>(isW ? &s_kbT[col][s0]
+                                                      : &s_vbT[col][s0]);
+          }
+          acc = isW ? mfma_bf16(bv, iv, acc)   // W^T tile: rows c, cols r
+                    : mfma_bf16(iv, bv, acc);  // U~ tile: rows r, cols j
+        }
+        bf16x4 ov;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = (bf16)acc[i];
+        if (isW) {
+          *reinterpret_cast<bf16x4*>(gW + r * K + 16 * ct + 4 * kg) = ov;
+        } else {
+          *reinterpret_cast<bf16x4*>(gUtT + col * C + 16 * m + 4 * kg) = ov;
+        }
       }
     }
   }
 }
 
+// Persistent launch: as many workgroups as fit on the device at once, each
+// walking the work items with a stride of the grid size.
 template <typename Tin, int D, int C>
 hipError_t launch(const PrefillArgs& a, hipStream_t st) {
-  dim3 grid((unsigned)a.max_chunks, (unsigned)a.H, (unsigned)a.N);
-  return launch_kernel(prep_kernel<Tin, D, C>, grid, dim3(256), st, a);
+  const int64_t items = (int64_t)a.N * a.max_chunks * a.H;
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess)
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void*>(prep_kernel<Tin, D, C>), 256, 0);
+  if (e != hipSuccess) return e;
+  const int64_t resident = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+  const unsigned grid = (unsigned)(items < resident ? items : resident);
+  void* args[] = {const_cast<PrefillArgs*>(&a), const_cast<int64_t*>(&items)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(prep_kernel<Tin, D, C>),
+                         dim3(grid), dim3(256), args, 0, st);
 }
 
 template <typename Tin, int D>

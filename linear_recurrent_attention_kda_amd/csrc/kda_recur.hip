@@ -26,6 +26,19 @@
 namespace kda {
 namespace {
 
+// Operands of one chunk that one wave needs, loaded straight into registers
+// in MFMA operand layout.  Wave w owns U/O row tile m (all its jt tiles) and
+// state tiles ct0 .. ct0 + NCT - 1, so no two waves of a workgroup load the
+// same bytes.
+template <int KSTEPS, int CSTEPS, int UPW, int NCT>
+struct ChunkOps {
+  bf16x8 w[KSTEPS], qh[KSTEPS];   // rows of W and Q^ (row tile m)
+  bf16x8 m[CSTEPS];               // row tile m of M
+  bf16x8 kb[NCT][CSTEPS];         // rows of K-bar^T (state row tiles)
+  uint2 ut[UPW];                  // U~^T, 4 rows of one column per tile
+  float4 gm[NCT];                 // gamma for the 4 state rows of the lane
+};
+
 template <typename Tout, int D, int C, int BV>
 __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
   constexpr int K = D, V = D;
@@ -36,9 +49,13 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
   constexpr int MT = C / 16;               // 16-row tiles of a chunk
   constexpr int NUT = MT * JT;             // U / O tiles per chunk
   constexpr int UPW = (NUT + 3) / 4;       // U / O tiles per wave
+  constexpr int NCT = SPW >= JT ? SPW / JT : 1;  // state row tiles per wave
   constexpr int KSTEPS = (K + 31) / 32;
+  constexpr int CSTEPS = (C + 31) / 32;
   constexpr int SP = K + 8, UP = C + 8;    // padded LDS strides (bf16)
   static_assert(V % BV == 0 && BV % 16 == 0, "slice width");
+  static_assert(UPW <= JT && (SPW % JT == 0 || SPW < JT), "wave tiling");
+  using Ops = ChunkOps<KSTEPS, CSTEPS, UPW, NCT>;
 
   __shared__ __attribute__((aligned(16))) bf16 s_SbT[BV][SP];  // S^T, bf16
   __shared__ __attribute__((aligned(16))) bf16 s_UbT[BV][UP];  // U^T, bf16
@@ -60,13 +77,20 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rl = lane & 15, kg = lane >> 4;
 
-  // ---- initial state -> accumulators (D layout: row c = 16ct + 4kg + i,
+  // this wave's tiles
+  const int u0 = wave * UPW;                 // first U/O tile
+  const bool has_u = u0 < NUT;
+  const int mrow = has_u ? u0 / JT : 0;      // its row tile
+  const int s0t = wave * SPW;                // first state tile
+  const int ct0 = s0t / JT;
+
+  // ---- initial state -> accumulators (D layout: row c = 16ct + 4kg + e,
   //      column j = 16jt + rl) and its bf16 copy -----------------------------
   f32x4 S[SPW];
   const size_t sbase = ((size_t)n * H + h) * (size_t)K * V;
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
-    const int t = wave + 4 * i;
+    const int t = s0t + i;
     S[i] = zero4();
     if (t < NST) {
       const int ct = t / JT, jt = t % JT;
@@ -82,99 +106,136 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
       *reinterpret_cast<bf16x4*>(&s_SbT[16 * jt + rl][16 * ct + 4 * kg]) = sb;
     }
   }
-  __syncthreads();
 
-  Tout* o = static_cast<Tout*>(a.o);
   const int64_t nchunks = (eos - bos + C - 1) / C;
-  for (int64_t ci = 0; ci < nchunks; ++ci) {
-    const int64_t t0 = bos + ci * C;
-    const int L = (eos - t0) < C ? (int)(eos - t0) : C;
-    const int64_t slot = t0 / C + n;
-    const char* blk = a.ws + ((size_t)h * a.nslots + slot) * lay.block_bytes;
+  const char* ws_head = a.ws + (size_t)h * a.nslots * lay.block_bytes;
+
+  // Issue the loads of chunk ci's operands (nothing if ci is past the end).
+  auto load_ops = [&](Ops& op, int64_t ci) {
+    if (ci >= nchunks) return;
+    const int64_t slot = (bos + ci * C) / C + n;
+    const char* blk = ws_head + (size_t)slot * lay.block_bytes;
     const bf16* gW = reinterpret_cast<const bf16*>(blk + lay.off_W);
     const bf16* gQh = reinterpret_cast<const bf16*>(blk + lay.off_Qh);
     const bf16* gKbT = reinterpret_cast<const bf16*>(blk + lay.off_KbT);
     const bf16* gUtT = reinterpret_cast<const bf16*>(blk + lay.off_UtT);
     const bf16* gM = reinterpret_cast<const bf16*>(blk + lay.off_M);
-    const float* gGamma = reinterpret_cast<const float*>(blk + lay.off_gamma);
-
-    // ---- U = U~ - W S  and  O^T = S^T Q^^T  (O kept transposed) -----------
-    f32x4 Ot[UPW];
+    const float* gG = reinterpret_cast<const float*>(blk + lay.off_gamma);
+    if (has_u) {
 #pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-      const int u = wave + 4 * i;
-      Ot[i] = zero4();
-      if (u < NUT) {
-        const int m = u / JT, jt = u % JT;
-        f32x4 ws = zero4();
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          const int c0 = 32 * kk + 8 * kg;
-          bf16x8 w = zero_bf16x8(), qh = zero_bf16x8(), sb = zero_bf16x8();
-          if (c0 < K) {
-            w = load_bf16x8(gW + (16 * m + rl) * K + c0);
-            qh = load_bf16x8(gQh + (16 * m + rl) * K + c0);
-            sb = *reinterpret_cast<const bf16x8*>(&s_SbT[16 * jt + rl][c0]);
-          }
-          ws = mfma_bf16(w, sb, ws);          // (W S) tile: rows r, cols j
-          Ot[i] = mfma_bf16(sb, qh, Ot[i]);   // (Q^ S)^T tile: rows j, cols r
-        }
-        // U~^T[j][r .. r+3], r = 16m + 4kg
-        const uint2 raw = *reinterpret_cast<const uint2*>(
-            gUtT + (j0 + 16 * jt + rl) * C + 16 * m + 4 * kg);
-        const bf16x4 ut = __builtin_bit_cast(bf16x4, raw);
-        bf16x4 ub;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ub[e] = (bf16)((float)ut[e] - ws[e]);
-        *reinterpret_cast<bf16x4*>(&s_UbT[16 * jt + rl][16 * m + 4 * kg]) = ub;
-      }
-    }
-    __syncthreads();
-
-    // ---- O^T += U^T M^T, store O ------------------------------------------
-#pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-      const int u = wave + 4 * i;
-      if (u < NUT) {
-        const int m = u / JT, jt = u % JT;
-        const int csteps = (16 * (m + 1) + 31) / 32;
-        for (int cs = 0; cs < csteps; ++cs) {
-          const int s0 = 32 * cs + 8 * kg;
-          bf16x8 mb = zero_bf16x8(), ubv = zero_bf16x8();
-          if (s0 < C) {
-            mb = load_bf16x8(gM + (16 * m + rl) * C + s0);
-            ubv = *reinterpret_cast<const bf16x8*>(&s_UbT[16 * jt + rl][s0]);
-          }
-          Ot[i] = mfma_bf16(ubv, mb, Ot[i]);
-        }
-        // O^T tile element (j = 16jt + 4kg + e, r = 16m + rl)
-        const int r = 16 * m + rl;
-        if (r < L) {
-          store4(o + ((t0 + r) * H + h) * (int64_t)V + j0 + 16 * jt + 4 * kg,
-                 Ot[i], a.scale);
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const int c0 = 32 * kk + 8 * kg;
+        if (c0 < K) {
+          op.w[kk] = load_bf16x8(gW + (16 * mrow + rl) * K + c0);
+          op.qh[kk] = load_bf16x8(gQh + (16 * mrow + rl) * K + c0);
         }
       }
-    }
-
-    // ---- S <- diag(gamma) S + K-bar^T U -------------------------------------
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-      const int t = wave + 4 * i;
-      if (t < NST) {
-        const int ct = t / JT, jt = t % JT;
-        const float4 gm =
-            *reinterpret_cast<const float4*>(gGamma + 16 * ct + 4 * kg);
-        S[i][0] *= gm.x; S[i][1] *= gm.y; S[i][2] *= gm.z; S[i][3] *= gm.w;
-        constexpr int CSTEPS = (C + 31) / 32;
+      for (int cs = 0; cs < CSTEPS; ++cs) {
+        const int s0 = 32 * cs + 8 * kg;
+        if (s0 < C && s0 < 16 * (mrow + 1))
+          op.m[cs] = load_bf16x8(gM + (16 * mrow + rl) * C + s0);
+      }
+#pragma unroll
+      for (int i = 0; i < UPW; ++i) {
+        const int jt = (u0 + i) % JT;
+        if (u0 + i < NUT)
+          op.ut[i] = *reinterpret_cast<const uint2*>(
+              gUtT + (j0 + 16 * jt + rl) * C + 16 * mrow + 4 * kg);
+      }
+    }
+#pragma unroll
+    for (int lc = 0; lc < NCT; ++lc) {
+      const int ct = ct0 + lc;
+      if (ct < KT && s0t < NST) {
 #pragma unroll
         for (int cs = 0; cs < CSTEPS; ++cs) {
           const int s0 = 32 * cs + 8 * kg;
-          bf16x8 kb = zero_bf16x8(), ubv = zero_bf16x8();
-          if (s0 < C) {
-            kb = load_bf16x8(gKbT + (16 * ct + rl) * C + s0);
-            ubv = *reinterpret_cast<const bf16x8*>(&s_UbT[16 * jt + rl][s0]);
+          if (s0 < C) op.kb[lc][cs] = load_bf16x8(gKbT + (16 * ct + rl) * C + s0);
+        }
+        op.gm[lc] = *reinterpret_cast<const float4*>(gG + 16 * ct + 4 * kg);
+      }
+    }
+  };
+
+  Tout* o = static_cast<Tout*>(a.o);
+
+  // One chunk of the recurrence with its operands already in registers.
+  auto process = [&](const Ops& op, int64_t ci) {
+    const int64_t t0 = bos + ci * C;
+    const int L = (eos - t0) < C ? (int)(eos - t0) : C;
+    __syncthreads();  // S^T copy complete; U^T buffer free
+
+    // U = U~ - W S,  O^T = S^T Q^^T
+    f32x4 Ot[UPW];
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      Ot[i] = zero4();
+      if (u0 + i < NUT) {
+        const int jt = (u0 + i) % JT;
+        f32x4 wsacc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          // per-lane guards only select operands; every lane runs the MFMA
+          const int c0 = 32 * kk + 8 * kg;
+          bf16x8 sb = zero_bf16x8();
+          if (c0 < K)
+            sb = *reinterpret_cast<const bf16x8*>(&s_SbT[16 * jt + rl][c0]);
+          wsacc = mfma_bf16(op.w[kk], sb, wsacc);
+          Ot[i] = mfma_bf16(sb, op.qh[kk], Ot[i]);
+        }
+        const bf16x4 ut = __builtin_bit_cast(bf16x4, op.ut[i]);
+        bf16x4 ub;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ub[e] = (bf16)((float)ut[e] - wsacc[e]);
+        *reinterpret_cast<bf16x4*>(&s_UbT[16 * jt + rl][16 * mrow + 4 * kg]) =
+            ub;
+      }
+    }
+    __syncthreads();  // U^T complete
+
+    // O^T += U^T M^T; store O
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      if (u0 + i < NUT) {
+        const int jt = (u0 + i) % JT;
+#pragma unroll
+        for (int cs = 0; cs < CSTEPS; ++cs) {
+          if (32 * cs < 16 * (mrow + 1)) {  // uniform: M is lower triangular
+            const int s0 = 32 * cs + 8 * kg;
+            bf16x8 ubv = zero_bf16x8();
+            if (s0 < C)
+              ubv = *reinterpret_cast<const bf16x8*>(&s_UbT[16 * jt + rl][s0]);
+            Ot[i] = mfma_bf16(ubv, op.m[cs], Ot[i]);
           }
-          S[i] = mfma_bf16(kb, ubv, S[i]);
+        }
+        const int r = 16 * mrow + rl;
+        if (r < L)
+          store4(o + ((t0 + r) * H + h) * (int64_t)V + j0 + 16 * jt + 4 * kg,
+                 Ot[i], a.scale);
+      }
+    }
+
+    // S <- diag(gamma) S + K-bar^T U
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      const int t = s0t + i;
+      if (t < NST) {
+        // tiles s0t .. s0t + SPW - 1 cover whole rows ct0 .. ct0 + NCT - 1
+        // (or part of one row when SPW < JT)
+        constexpr bool kRows = SPW >= JT;
+        const int lc = kRows ? i / JT : 0;
+        const int jt = kRows ? i % JT : t % JT;
+        const int ct = ct0 + lc;
+        const float4 gm = op.gm[lc];
+        S[i][0] *= gm.x; S[i][1] *= gm.y; S[i][2] *= gm.z; S[i][3] *= gm.w;
+#pragma unroll
+        for (int cs = 0; cs < CSTEPS; ++cs) {
+          const int s0 = 32 * cs + 8 * kg;
+          bf16x8 ubv = zero_bf16x8();
+          if (s0 < C)
+            ubv = *reinterpret_cast<const bf16x8*>(&s_UbT[16 * jt + rl][s0]);
+          S[i] = mfma_bf16(op.kb[lc][cs], ubv, S[i]);
         }
         bf16x4 sb;
 #pragma unroll
@@ -182,13 +243,42 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
         *reinterpret_cast<bf16x4*>(&s_SbT[16 * jt + rl][16 * ct + 4 * kg]) = sb;
       }
     }
-    __syncthreads();
+  };
+
+  // Two register sets: chunk ci computes while chunk ci + 1 is in flight;
+  // the set freed by ci is refilled with ci + 2.
+  Ops opA, opB;
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    opA.w[kk] = opA.qh[kk] = opB.w[kk] = opB.qh[kk] = zero_bf16x8();
+  }
+#pragma unroll
+  for (int cs = 0; cs < CSTEPS; ++cs) {
+    opA.m[cs] = opB.m[cs] = zero_bf16x8();
+#pragma unroll
+    for (int lc = 0; lc < NCT; ++lc) opA.kb[lc][cs] = opB.kb[lc][cs] = zero_bf16x8();
+  }
+#pragma unroll
+  for (int i = 0; i < UPW; ++i) opA.ut[i] = opB.ut[i] = make_uint2(0u, 0u);
+#pragma unroll
+  for (int lc = 0; lc < NCT; ++lc)
+    opA.gm[lc] = opB.gm[lc] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  load_ops(opA, 0);
+  load_ops(opB, 1);
+  for (int64_t ci = 0; ci < nchunks; ci += 2) {
+    process(opA, ci);
+    load_ops(opA, ci + 2);
+    if (ci + 1 < nchunks) {
+      process(opB, ci + 1);
+      load_ops(opB, ci + 3);
+    }
   }
 
   if (a.final_state) {
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-      const int t = wave + 4 * i;
+      const int t = s0t + i;
       if (t < NST) {
         const int ct = t / JT, jt = t % JT;
 #pragma unroll
