@@ -104,6 +104,35 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 acc) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Buffer resource over [base, base + bytes): buffer loads past the end
+// return 0 and buffer stores past the end are dropped by the hardware, which
+// lets partial chunks use the same unconditional memory instructions as
+// full ones.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes,
+                                           0x00020000);
+}
+// Four elements x * scale at byte offset `off` of buffer r.
+__device__ __forceinline__ void buffer_store4(bf16*, __amdgpu_buffer_rsrc_t r,
+                                              uint32_t off, f32x4 x,
+                                              float scale) {
+  bf16x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = (bf16)(x[i] * scale);
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off,
+                                        0, 0);
+}
+__device__ __forceinline__ void buffer_store4(float*, __amdgpu_buffer_rsrc_t r,
+                                              uint32_t off, f32x4 x,
+                                              float scale) {
+  const f32x4 v = x * scale;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off,
+                                         0, 0);
+}
+
 // Four consecutive storage-dtype elements (8-byte aligned for bf16, 16-byte
 // for fp32) from x * scale.
 __device__ __forceinline__ void store4(bf16* p, f32x4 x, float scale) {

@@ -83,6 +83,16 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
   const int mrow = has_u ? u0 / JT : 0;      // its row tile
   const int s0t = wave * SPW;                // first state tile
   const int ct0 = s0t / JT;
+  const bool has_s = s0t < NST;
+
+  // For the production shapes every lane guard below is a compile-time
+  // "true", so the loop's loads and stores are branch-free and the compiler
+  // can count outstanding memory operations exactly (a branch makes it wait
+  // for all of them, which would serialise the prefetch).
+  constexpr bool kFullK = K % 32 == 0;      // every lane's column group < K
+  constexpr bool kFullC = C % 32 == 0;      // every lane's row group < C
+  constexpr bool kAllU = NUT % 4 == 0;      // every wave owns U/O tiles
+  constexpr bool kAllS = NST % 4 == 0;      // every wave owns state tiles
 
   // ---- initial state -> accumulators (D layout: row c = 16ct + 4kg + e,
   //      column j = 16jt + rl) and its bf16 copy -----------------------------
@@ -110,9 +120,10 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
   const int64_t nchunks = (eos - bos + C - 1) / C;
   const char* ws_head = a.ws + (size_t)h * a.nslots * lay.block_bytes;
 
-  // Issue the loads of chunk ci's operands (nothing if ci is past the end).
+  // Issue the loads of chunk ci's operands.  ci is clamped to the last
+  // chunk (a harmless duplicate load) instead of branching.
   auto load_ops = [&](Ops& op, int64_t ci) {
-    if (ci >= nchunks) return;
+    ci = ci < nchunks ? ci : nchunks - 1;
     const int64_t slot = (bos + ci * C) / C + n;
     const char* blk = ws_head + (size_t)slot * lay.block_bytes;
     const bf16* gW = reinterpret_cast<const bf16*>(blk + lay.off_W);
@@ -121,37 +132,38 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
     const bf16* gUtT = reinterpret_cast<const bf16*>(blk + lay.off_UtT);
     const bf16* gM = reinterpret_cast<const bf16*>(blk + lay.off_M);
     const float* gG = reinterpret_cast<const float*>(blk + lay.off_gamma);
-    if (has_u) {
+    if (kAllU || has_u) {
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
         const int c0 = 32 * kk + 8 * kg;
-        if (c0 < K) {
+        if (kFullK || c0 < K) {
           op.w[kk] = load_bf16x8(gW + (16 * mrow + rl) * K + c0);
           op.qh[kk] = load_bf16x8(gQh + (16 * mrow + rl) * K + c0);
         }
       }
 #pragma unroll
       for (int cs = 0; cs < CSTEPS; ++cs) {
-        const int s0 = 32 * cs + 8 * kg;
-        if (s0 < C && s0 < 16 * (mrow + 1))
+        const int s0 = 32 * cs + 8 * kg;   // M is zero above the diagonal
+        if (kFullC || s0 < C)
           op.m[cs] = load_bf16x8(gM + (16 * mrow + rl) * C + s0);
       }
 #pragma unroll
       for (int i = 0; i < UPW; ++i) {
         const int jt = (u0 + i) % JT;
-        if (u0 + i < NUT)
+        if (kAllU || u0 + i < NUT)
           op.ut[i] = *reinterpret_cast<const uint2*>(
               gUtT + (j0 + 16 * jt + rl) * C + 16 * mrow + 4 * kg);
       }
     }
+    if (kAllS || has_s) {
 #pragma unroll
-    for (int lc = 0; lc < NCT; ++lc) {
-      const int ct = ct0 + lc;
-      if (ct < KT && s0t < NST) {
+      for (int lc = 0; lc < NCT; ++lc) {
+        const int ct = ct0 + lc;
 #pragma unroll
         for (int cs = 0; cs < CSTEPS; ++cs) {
           const int s0 = 32 * cs + 8 * kg;
-          if (s0 < C) op.kb[lc][cs] = load_bf16x8(gKbT + (16 * ct + rl) * C + s0);
+          if (kFullC || s0 < C)
+            op.kb[lc][cs] = load_bf16x8(gKbT + (16 * ct + rl) * C + s0);
         }
         op.gm[lc] = *reinterpret_cast<const float4*>(gG + 16 * ct + 4 * kg);
       }
@@ -164,6 +176,10 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
   auto process = [&](const Ops& op, int64_t ci) {
     const int64_t t0 = bos + ci * C;
     const int L = (eos - t0) < C ? (int)(eos - t0) : C;
+    // outputs of this chunk and slice: rows r < L at stride H*V elements
+    const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(
+        o + (t0 * H + h) * (int64_t)V + j0,
+        (uint32_t)(((int64_t)(L - 1) * H * V + BV) * sizeof(Tout)));
     __syncthreads();  // S^T copy complete; U^T buffer free
 
     // U = U~ - W S,  O^T = S^T Q^^T
@@ -171,7 +187,7 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
       Ot[i] = zero4();
-      if (u0 + i < NUT) {
+      if (kAllU || u0 + i < NUT) {
         const int jt = (u0 + i) % JT;
         f32x4 wsacc = zero4();
 #pragma unroll
@@ -179,7 +195,7 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
           // per-lane guards only select operands; every lane runs the MFMA
           const int c0 = 32 * kk + 8 * kg;
           bf16x8 sb = zero_bf16x8();
-          if (c0 < K)
+          if (kFullK || c0 < K)
             sb = *reinterpret_cast<const bf16x8*>(&s_SbT[16 * jt + rl][c0]);
           wsacc = mfma_bf16(op.w[kk], sb, wsacc);
           Ot[i] = mfma_bf16(sb, op.qh[kk], Ot[i]);
@@ -194,25 +210,24 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
     }
     __syncthreads();  // U^T complete
 
-    // O^T += U^T M^T; store O
+    // O^T += U^T M^T; store O (rows >= L fall outside the buffer: dropped)
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
-      if (u0 + i < NUT) {
+      if (kAllU || u0 + i < NUT) {
         const int jt = (u0 + i) % JT;
 #pragma unroll
         for (int cs = 0; cs < CSTEPS; ++cs) {
-          if (32 * cs < 16 * (mrow + 1)) {  // uniform: M is lower triangular
-            const int s0 = 32 * cs + 8 * kg;
-            bf16x8 ubv = zero_bf16x8();
-            if (s0 < C)
-              ubv = *reinterpret_cast<const bf16x8*>(&s_UbT[16 * jt + rl][s0]);
-            Ot[i] = mfma_bf16(ubv, op.m[cs], Ot[i]);
-          }
+          const int s0 = 32 * cs + 8 * kg;
+          bf16x8 ubv = zero_bf16x8();
+          if (kFullC || s0 < C)
+            ubv = *reinterpret_cast<const bf16x8*>(&s_UbT[16 * jt + rl][s0]);
+          Ot[i] = mfma_bf16(ubv, op.m[cs], Ot[i]);
         }
         const int r = 16 * mrow + rl;
-        if (r < L)
-          store4(o + ((t0 + r) * H + h) * (int64_t)V + j0 + 16 * jt + 4 * kg,
-                 Ot[i], a.scale);
+        buffer_store4(o, orsrc,
+                      (uint32_t)(((int64_t)r * H * V + 16 * jt + 4 * kg) *
+                                 sizeof(Tout)),
+                      Ot[i], a.scale);
       }
     }
 
@@ -220,7 +235,7 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const int t = s0t + i;
-      if (t < NST) {
+      if (kAllS || t < NST) {
         // tiles s0t .. s0t + SPW - 1 cover whole rows ct0 .. ct0 + NCT - 1
         // (or part of one row when SPW < JT)
         constexpr bool kRows = SPW >= JT;
@@ -233,7 +248,7 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
         for (int cs = 0; cs < CSTEPS; ++cs) {
           const int s0 = 32 * cs + 8 * kg;
           bf16x8 ubv = zero_bf16x8();
-          if (s0 < C)
+          if (kFullC || s0 < C)
             ubv = *reinterpret_cast<const bf16x8*>(&s_UbT[16 * jt + rl][s0]);
           S[i] = mfma_bf16(op.kb[lc][cs], ubv, S[i]);
         }
@@ -264,15 +279,20 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
   for (int lc = 0; lc < NCT; ++lc)
     opA.gm[lc] = opB.gm[lc] = make_float4(0.f, 0.f, 0.f, 0.f);
 
-  load_ops(opA, 0);
-  load_ops(opB, 1);
-  for (int64_t ci = 0; ci < nchunks; ci += 2) {
-    process(opA, ci);
-    load_ops(opA, ci + 2);
-    if (ci + 1 < nchunks) {
+  // The pair loop has no branch in its body, so both paths into its header
+  // agree on the order of outstanding loads and the compiler waits only for
+  // the set it is about to use.
+  if (nchunks > 0) {
+    load_ops(opA, 0);
+    load_ops(opB, 1);
+    int64_t ci = 0;
+    for (; ci + 1 < nchunks; ci += 2) {
+      process(opA, ci);
+      load_ops(opA, ci + 2);
       process(opB, ci + 1);
       load_ops(opB, ci + 3);
     }
+    if (ci < nchunks) process(opA, ci);
   }
 
   if (a.final_state) {
