@@ -50,6 +50,11 @@ template <> struct Raw8<bf16> {
   __device__ __forceinline__ void load(const bf16* p) {
     v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
   }
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r,
+                                           uint32_t off) {
+    v = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
   __device__ __forceinline__ void zero() {
     v = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
   }
@@ -64,6 +69,13 @@ template <> struct Raw8<float> {
     lo = *reinterpret_cast<const float4*>(p);
     hi = *reinterpret_cast<const float4*>(p + 4);
   }
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r,
+                                           uint32_t off) {
+    lo = __builtin_bit_cast(
+        float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    hi = __builtin_bit_cast(
+        float4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+  }
   __device__ __forceinline__ void zero() {
     lo = hi = make_float4(0.f, 0.f, 0.f, 0.f);
   }
@@ -72,6 +84,30 @@ template <> struct Raw8<float> {
     x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
   }
 };
+
+// Eight consecutive elements of an LDS row (bf16 or fp32) as floats, and
+// the reverse.
+__device__ __forceinline__ void lds_get8(const bf16* p, float (&x)[8]) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
+}
+__device__ __forceinline__ void lds_get8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void lds_put8(bf16* p, const float (&x)[8]) {
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (bf16)x[i];
+  *reinterpret_cast<bf16x8*>(p) = v;
+}
+__device__ __forceinline__ void lds_put8(float* p, const float (&x)[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
 
 __device__ __forceinline__ bf16x8 pack8(const float (&x)[8]) {
   bf16x8 r;
@@ -115,6 +151,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes,
                                            0x00020000);
 }
+// Raw buffer loads (out-of-range -> 0).
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r,
+                                                 uint32_t off) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ uint4 buffer_load_16(__amdgpu_buffer_rsrc_t r,
+                                                uint32_t off) {
+  return __builtin_bit_cast(uint4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // Four elements x * scale at byte offset `off` of buffer r.
 __device__ __forceinline__ void buffer_store4(bf16*, __amdgpu_buffer_rsrc_t r,
                                               uint32_t off, f32x4 x,

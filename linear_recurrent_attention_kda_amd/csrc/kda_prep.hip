@@ -31,6 +31,8 @@
 // 16-row sub-tile m.  Products use v_mfma_f32_16x16x32_bf16 (A, M, W, U~)
 // and v_mfma_f32_16x16x4_f32 (the off-diagonal blocks of INV).  Outputs are
 // written in the layouts the recurrence kernel reads as MFMA operands.
+#include <type_traits>
+
 #include "kda_device.hpp"
 
 namespace kda {
@@ -61,30 +63,46 @@ __device__ __forceinline__ Item decode_item(const PrefillArgs& a, int C,
 }
 
 template <typename Tin, int D, int C>
-__global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a,
+__global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
                                                    int64_t total_items) {
+  constexpr int NT = 512, NW = NT / 64;    // threads, waves
   constexpr int K = D, V = D;
   constexpr int NSUB = C / 16;             // 16-row sub-tiles per chunk
   constexpr int KSTEPS = (K + 31) / 32;    // 32-wide column groups of a row
-  constexpr int TPC = 256 / K;             // scan threads per channel
+  constexpr int TPC = (NT / K) < C ? (NT / K) : C;  // scan threads / channel
   constexpr int RPT = C / TPC;             // rows per scan thread
-  constexpr int AP = K + 4;                // padded strides (bank spread)
-  constexpr int CP = C + 4;
-  constexpr int TP = C + 8;
-  constexpr int KP = K + 8;
-  static_assert(NSUB >= 1 && NSUB <= 4 && C % TPC == 0 && K <= 256, "shape");
-  constexpr int ABUF = C * (AP > CP ? AP : CP);
+  constexpr int SCAN_T = TPC * K;          // threads taking part in the scan
+  constexpr int NPIECE = C * K / 8;        // 8-element pieces of q, k, v
+  constexpr int PPT = (NPIECE + NT - 1) / NT;
+  constexpr int NPAIR = NSUB * (NSUB + 1) / 2;  // (m, n <= m) tile pairs
+  constexpr int NUP = NSUB * (NSUB - 1) / 2;    // (m, n > m): M is zero there
+  constexpr int KT = K / 16, VT = V / 16;
+  constexpr int NTILE = NSUB * (KT + VT);  // W^T and U~ output tiles
+  constexpr int TPW = (NTILE + NW - 1) / NW;
+  constexpr int AP = K + 4, CP = C + 4, TP = C + 8, KP = K + 8;
+  static_assert(NSUB >= 1 && NSUB <= 4 && C % TPC == 0 && K <= 512, "shape");
+  static_assert(NUP <= NW && NPAIR <= 2 * NW, "work split");
+  // fp32 inputs at large head dims are staged as bf16 to fit LDS; every
+  // product they feed takes bf16 operands anyway.
+  using Lt = typename std::conditional<(sizeof(Tin) == 4 && D >= 64), bf16,
+                                       Tin>::type;
+  constexpr bool kFullScan = SCAN_T == NT;
+  constexpr bool kFullPieces = NPIECE % NT == 0;
+  constexpr bool kFullK = K % 32 == 0;
 
   // s_a (cumulative log2-decay) is dead once A and M are formed; the
   // inverse then reuses its storage.
+  constexpr int ABUF = C * (AP > CP ? AP : CP);
   __shared__ __attribute__((aligned(16))) float s_abuf[ABUF];
   float (*s_a)[AP] = reinterpret_cast<float (*)[AP]>(s_abuf);
   float (*s_inv)[CP] = reinterpret_cast<float (*)[CP]>(s_abuf);
-  __shared__ float s_A[C][CP];             // beta-scaled strictly-lower A
-  __shared__ __attribute__((aligned(16))) Tin s_k[C][KP];     // k rows
+  __shared__ float s_A[C][CP];                                // beta-scaled A
+  __shared__ __attribute__((aligned(16))) Lt s_q[C][KP];      // q rows
+  __shared__ __attribute__((aligned(16))) Lt s_k[C][KP];      // k rows
   __shared__ __attribute__((aligned(16))) bf16 s_kbT[K][TP];  // (beta k e^a)^T
   __shared__ __attribute__((aligned(16))) bf16 s_vbT[V][TP];  // (beta v)^T
-  __shared__ float s_tmp[4][16][20];
+  __shared__ __attribute__((aligned(16))) bf16 s_invb[C][TP]; // INV, bf16
+  __shared__ float s_tmp[NW][16][20];
   __shared__ float s_beta[C];
   __shared__ float s_tot[TPC][K];
 
@@ -92,75 +110,83 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rl = lane & 15, kg = lane >> 4;
   const int sc = tid % K, sseg = tid / K;  // scan layout
-  const int rrow = 16 * wave + rl;         // row-operand layout row
-  const bool has_row = wave < NSUB;
   const Tin* qg = static_cast<const Tin*>(a.q);
   const Tin* kgp = static_cast<const Tin*>(a.k);
   const Tin* vg = static_cast<const Tin*>(a.v);
   const WsLayout lay = WsLayout::make(C, K, V);
 
-  // Prefetch registers (one item ahead).  g in the scan layout; q, k, v in
-  // the row-operand layout (row 16*wave + lane%16, columns 32ks + 8kg).
-  float rg[RPT];
-  Raw8<Tin> rq[KSTEPS], rk[KSTEPS], rv[KSTEPS];
-  float rbeta = 0.f;
+  // Blocks of INV above the diagonal are never written: zero their bf16
+  // copy once.
+  for (int e = tid; e < C * C; e += NT) {
+    const int r = e / C, c = e % C;
+    if (c / 16 > r / 16) s_invb[r][c] = (bf16)0.f;
+  }
 
-  auto load_gvb = [&](const Item& it) {
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int r = sseg * RPT + i;
-      rg[i] = r < it.L ? a.g[((it.t0 + r) * H + it.h) * (int64_t)K + sc] : 0.f;
-    }
-    const bool row = has_row && rrow < it.L;
-    rbeta = row ? a.beta[(it.t0 + rrow) * H + it.h] : 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int c0 = 32 * ks + 8 * kg;
-      if (row && c0 < V)
-        rv[ks].load(vg + ((it.t0 + rrow) * H + it.h) * (int64_t)V + c0);
-      else
-        rv[ks].zero();
-    }
+  // Input buffers of one item: rows t0 .. t0+L-1 of (token, head); rows past
+  // L fall outside the buffer and load as 0.
+  struct Rs {
+    __amdgpu_buffer_rsrc_t q, k, v, g, b;
   };
-  auto load_qk = [&](const Item& it) {
-    const bool row = has_row && rrow < it.L;
+  auto item_rsrc = [&](const Item& it) {
+    Rs r;
+    const int64_t row0 = it.t0 * H + it.h;
+    const int64_t span = (int64_t)(it.L - 1) * H;
+    r.q = make_rsrc(qg + row0 * K, (uint32_t)((span * K + K) * sizeof(Tin)));
+    r.k = make_rsrc(kgp + row0 * K, (uint32_t)((span * K + K) * sizeof(Tin)));
+    r.v = make_rsrc(vg + row0 * V, (uint32_t)((span * V + V) * sizeof(Tin)));
+    r.g = make_rsrc(a.g + row0 * K, (uint32_t)((span * K + K) * 4));
+    r.b = make_rsrc(a.beta + row0, (uint32_t)((span + 1) * 4));
+    return r;
+  };
+
+  // Prefetch registers, one item ahead: g in the scan layout (channel sc,
+  // rows sseg*RPT + i), q/k/v as 8-element pieces, beta of row tid.
+  float rg[RPT];
+  Raw8<Tin> rq[PPT], rk[PPT], rv[PPT];
+  float rbeta = 0.f;
+  auto load_inputs = [&](const Rs& R) {
+    if (kFullScan || tid < SCAN_T) {
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int c0 = 32 * ks + 8 * kg;
-      if (row && c0 < K) {
-        const int64_t base = ((it.t0 + rrow) * H + it.h) * (int64_t)K + c0;
-        rq[ks].load(qg + base);
-        rk[ks].load(kgp + base);
-      } else {
-        rq[ks].zero();
-        rk[ks].zero();
+      for (int i = 0; i < RPT; ++i)
+        rg[i] = buffer_load_f32(
+            R.g, (uint32_t)((((int64_t)(sseg * RPT + i) * H) * K + sc) * 4));
+    }
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int p = tid + NT * i;
+      if (kFullPieces || p < NPIECE) {
+        const int pr = p / (K / 8), c0 = 8 * (p % (K / 8));
+        const uint32_t off =
+            (uint32_t)(((int64_t)pr * H * K + c0) * sizeof(Tin));
+        rq[i].load_buf(R.q, off);
+        rk[i].load_buf(R.k, off);
+        rv[i].load_buf(R.v, off);
       }
     }
+    if (tid < C) rbeta = buffer_load_f32(R.b, (uint32_t)((int64_t)tid * H * 4));
   };
 
   int64_t item = blockIdx.x;
-  int64_t have = -1;  // item whose inputs the prefetch registers hold
+  bool have = false;  // prefetch registers hold `item`'s inputs
   if (item < total_items) {
     const Item it = decode_item(a, C, item);
     if (it.valid) {
-      load_gvb(it);
-      load_qk(it);
-      have = item;
+      load_inputs(item_rsrc(it));
+      have = true;
     }
   }
 
   for (; item < total_items; item += gridDim.x) {
     const Item it = decode_item(a, C, item);
     if (!it.valid) continue;  // uniform across the workgroup
-    if (have != item) {
-      load_gvb(it);
-      load_qk(it);
-    }
+    if (!have) load_inputs(item_rsrc(it));
     const int64_t next = item + gridDim.x;
     Item nx;
     nx.valid = false;
     if (next < total_items) nx = decode_item(a, C, next);
-    const int L = it.L;
+    have = nx.valid;
+    const Rs nrs = item_rsrc(nx.valid ? nx : it);  // harmless reload if none
+
     const int h = it.h;
     const int64_t slot = it.t0 / C + it.n;
     char* blk = a.ws + ((size_t)h * a.nslots + slot) * lay.block_bytes;
@@ -173,9 +199,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a,
 
     __syncthreads();  // the previous item is done with every LDS buffer
 
-    // ---- 1. stage: decay scan, beta, k rows, (beta v)^T ------------------
+    // ---- 1. stage: decay scan, beta, q and k rows, (beta v)^T ------------
     float loc[RPT];
-    {
+    if (kFullScan || tid < SCAN_T) {
       float run = 0.f;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
@@ -184,24 +210,21 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a,
       }
       s_tot[sseg][sc] = run;
     }
-    if (has_row) {
-      s_beta[rrow] = rbeta;
+    if (tid < C) s_beta[tid] = rbeta;
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int c0 = 32 * ks + 8 * kg;
-        if (c0 < K) {
-          *reinterpret_cast<Raw8<Tin>*>(&s_k[rrow][c0]) = rk[ks];
-        }
-        if (c0 < V) {
-          float x[8];
-          rv[ks].get(x);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) s_vbT[c0 + i][rrow] = (bf16)(rbeta * x[i]);
-        }
+    for (int i = 0; i < PPT; ++i) {
+      const int p = tid + NT * i;
+      if (kFullPieces || p < NPIECE) {
+        const int pr = p / (K / 8), c0 = 8 * (p % (K / 8));
+        float x[8];
+        rq[i].get(x);
+        lds_put8(&s_q[pr][c0], x);
+        rk[i].get(x);
+        lds_put8(&s_k[pr][c0], x);
       }
     }
     __syncthreads();
-    {
+    if (kFullScan || tid < SCAN_T) {
       float off = 0.f;
       for (int j = 0; j < sseg; ++j) off += s_tot[j][sc];
 #pragma unroll
@@ -209,119 +232,129 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a,
       if (sseg == TPC - 1)
         gGamma[sc] = __builtin_amdgcn_exp2f(loc[RPT - 1] + off);
     }
-    if (nx.valid) load_gvb(nx);  // g, v, beta registers are free now
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int p = tid + NT * i;
+      if (kFullPieces || p < NPIECE) {
+        const int pr = p / (V / 8), c0 = 8 * (p % (V / 8));
+        float x[8];
+        rv[i].get(x);
+        const float b = s_beta[pr];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_vbT[c0 + e][pr] = (bf16)(b * x[e]);
+      }
+    }
+    load_inputs(nrs);  // every prefetch register is free now
     __syncthreads();
 
-    // ---- 2. Q^ (from registers), K-bar^T (global) and (beta k e^a)^T -----
-    if (has_row) {
+    // ---- 2. Q^ and K-bar^T (workspace), (beta k e^a)^T (LDS) -------------
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int c0 = 32 * ks + 8 * kg;
-        if (c0 < K) {
-          float x[8];
-          rq[ks].get(x);
+    for (int i = 0; i < PPT; ++i) {
+      const int p = tid + NT * i;
+      if (kFullPieces || p < NPIECE) {
+        const int pr = p / (K / 8), c0 = 8 * (p % (K / 8));
+        float x[8], av[8];
+        lds_get8(&s_q[pr][c0], x);
+        lds_get8(&s_a[pr][c0], av);
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
-            x[i] *= __builtin_amdgcn_exp2f(s_a[rrow][c0 + i]);
-          *reinterpret_cast<bf16x8*>(gQh + rrow * K + c0) = pack8(x);
-        }
+        for (int e = 0; e < 8; ++e) x[e] *= __builtin_amdgcn_exp2f(av[e]);
+        *reinterpret_cast<bf16x8*>(gQh + pr * K + c0) = pack8(x);
       }
     }
-    for (int e = tid; e < K * (C / 8); e += 256) {
-      const int c = e % K, s0 = 8 * (e / K);
-      const float alast = s_a[C - 1][c];
-      float kb[8], kh[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int s = s0 + i;
-        const float kv = io<Tin>::to_f(s_k[s][c]);
-        const float as = s_a[s][c];
-        kb[i] = kv * __builtin_amdgcn_exp2f(alast - as);
-        kh[i] = s_beta[s] * kv * __builtin_amdgcn_exp2f(as);
+    for (int i = 0; i < PPT; ++i) {
+      const int p = tid + NT * i;
+      if (kFullPieces || p < NPIECE) {
+        const int c = p % K, s0 = 8 * (p / K);
+        const float alast = s_a[C - 1][c];
+        float kb[8], kh[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int s = s0 + e;
+          const float kv = (float)s_k[s][c];
+          const float as = s_a[s][c];
+          kb[e] = kv * __builtin_amdgcn_exp2f(alast - as);
+          kh[e] = s_beta[s] * kv * __builtin_amdgcn_exp2f(as);
+        }
+        *reinterpret_cast<bf16x8*>(gKbT + c * C + s0) = pack8(kb);
+        *reinterpret_cast<bf16x8*>(&s_kbT[c][s0]) = pack8(kh);
       }
-      *reinterpret_cast<bf16x8*>(gKbT + c * C + s0) = pack8(kb);
-      *reinterpret_cast<bf16x8*>(&s_kbT[c][s0]) = pack8(kh);
     }
 
-    // ---- 3. A (LDS, fp32) and M (global, bf16) per 16-row sub-tile -------
-    if (has_row) {
-      const int m = wave;
-      bf16x8 kr[KSTEPS], qr[KSTEPS];
+    // ---- 3. A (LDS, fp32) and M (workspace, bf16): tile pairs (m, n <= m)
+    //         spread over the waves; zero tiles of M above the diagonal ----
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int c0 = 32 * ks + 8 * kg;
-        float kx[8], qx[8];
-        rk[ks].get(kx);
-        rq[ks].get(qx);
-        if (c0 < K) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float rho = m > 0 ? s_a[16 * m - 1][c0 + i] : 0.f;
-            const float f = __builtin_amdgcn_exp2f(s_a[rrow][c0 + i] - rho);
-            kx[i] *= f;
-            qx[i] *= f;
-          }
-        }
-        kr[ks] = pack8(kx);
-        qr[ks] = pack8(qx);
-      }
-      for (int nn = 0; nn < NSUB; ++nn) {
-        if (nn > m) {
-          // M is zero above the diagonal sub-tile.
-          *reinterpret_cast<uint2*>(gM + rrow * C + 16 * nn + 4 * kg) =
-              make_uint2(0u, 0u);
-          continue;
-        }
-        const int s = 16 * nn + rl;
+    for (int j = 0; j < 2; ++j) {
+      const int pidx = wave + NW * j;
+      if (pidx < NPAIR) {
+        int m = 0;
+        while ((m + 1) * (m + 2) / 2 <= pidx) ++m;
+        const int nn = pidx - m * (m + 1) / 2;
+        const int r = 16 * m + rl, s = 16 * nn + rl;
         f32x4 accA = zero4(), accMT = zero4();
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
           const int c0 = 32 * ks + 8 * kg;
-          float kx[8];
-          if (c0 < K) {
-            const Raw8<Tin> raw = *reinterpret_cast<const Raw8<Tin>*>(&s_k[s][c0]);
-            raw.get(kx);
+          float kx[8], qx[8], kc[8];
+          if (kFullK || c0 < K) {
+            float ar[8], as[8], rho[8];
+            lds_get8(&s_k[r][c0], kx);
+            lds_get8(&s_q[r][c0], qx);
+            lds_get8(&s_a[r][c0], ar);
+            lds_get8(&s_k[s][c0], kc);
+            lds_get8(&s_a[s][c0], as);
+            if (m > 0) {
+              lds_get8(&s_a[16 * m - 1][c0], rho);
+            } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const float rho = m > 0 ? s_a[16 * m - 1][c0 + i] : 0.f;
-              kx[i] *= __builtin_amdgcn_exp2f(rho - s_a[s][c0 + i]);
+              for (int e = 0; e < 8; ++e) rho[e] = 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float f = __builtin_amdgcn_exp2f(ar[e] - rho[e]);
+              kx[e] *= f;
+              qx[e] *= f;
+              kc[e] *= __builtin_amdgcn_exp2f(rho[e] - as[e]);
             }
           } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) kx[i] = 0.f;
+            for (int e = 0; e < 8; ++e) kx[e] = qx[e] = kc[e] = 0.f;
           }
-          const bf16x8 kc = pack8(kx);
-          accA = mfma_bf16(kr[ks], kc, accA);    // A tile: rows r, cols s
-          accMT = mfma_bf16(kc, qr[ks], accMT);  // M^T tile: rows s, cols r
+          const bf16x8 kcb = pack8(kc);
+          accA = mfma_bf16(pack8(kx), kcb, accA);    // A tile: rows r, cols s
+          accMT = mfma_bf16(kcb, pack8(qx), accMT);  // M^T tile: rows s, cols r
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = 16 * m + 4 * kg + i, ss = 16 * nn + rl;
-          s_A[rr][ss] = ss < rr ? s_beta[rr] * accA[i] : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 16 * m + 4 * kg + e, ss = 16 * nn + rl;
+          s_A[rr][ss] = ss < rr ? s_beta[rr] * accA[e] : 0.f;
         }
         bf16x4 mv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ss = 16 * nn + 4 * kg + i;
-          mv[i] = (bf16)(ss <= rrow ? accMT[i] : 0.f);
+        for (int e = 0; e < 4; ++e) {
+          const int ss = 16 * nn + 4 * kg + e;
+          mv[e] = (bf16)(ss <= r ? accMT[e] : 0.f);
         }
-        *reinterpret_cast<bf16x4*>(gM + rrow * C + 16 * nn + 4 * kg) = mv;
+        *reinterpret_cast<bf16x4*>(gM + r * C + 16 * nn + 4 * kg) = mv;
       }
     }
-    if (nx.valid) {
-      load_qk(nx);  // q, k registers are free now
-      have = next;
-    } else {
-      have = -1;
+    if (wave >= NW - NUP) {
+      int z = NW - 1 - wave, m = 0;  // z-th tile above the diagonal
+      while (z >= NSUB - 1 - m) {
+        z -= NSUB - 1 - m;
+        ++m;
+      }
+      const int nn = m + 1 + z;
+      *reinterpret_cast<uint2*>(gM + (16 * m + rl) * C + 16 * nn + 4 * kg) =
+          make_uint2(0u, 0u);
     }
-    __syncthreads();  // A complete; decay buffer no longer read
+    __syncthreads();  // A complete; the decay buffer is no longer read
 
-    // ---- 4. INV = (I + A)^-1: diagonal 16x16 blocks by forward
-    //         substitution (one column per lane), then off-diagonal blocks by
-    //         levels: INV_mn = -INV_mm * sum_{j=n}^{m-1} A_mj INV_jn ---------
-    for (int i = tid; i < C * CP; i += 256) (&s_inv[0][0])[i] = 0.f;
-    __syncthreads();
-    if (has_row && lane < 16) {
+    // ---- 4. INV = (I + A)^-1 in fp32 (s_inv) and bf16 (s_invb): diagonal
+    //         16x16 blocks by forward substitution (one column per lane),
+    //         then off-diagonal blocks by levels:
+    //         INV_mn = -INV_mm * sum_{j=n}^{m-1} A_mj INV_jn ----------------
+    if (wave < NSUB && lane < 16) {
       const int m = wave, j = lane, b = 16 * m;
       float x[16];
 #pragma unroll
@@ -332,7 +365,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a,
         x[r] = acc;
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_inv[b + r][b + j] = x[r];
+      for (int r = 0; r < 16; ++r) {
+        s_inv[b + r][b + j] = x[r];
+        s_invb[b + r][b + j] = (bf16)x[r];
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -347,25 +383,27 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a,
                          s_inv[16 * j + 4 * kk + kg][16 * nb + rl], t);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_tmp[wave][4 * kg + i][rl] = t[i];
+        for (int e = 0; e < 4; ++e) s_tmp[wave][4 * kg + e][rl] = t[e];
         f32x4 u = zero4();
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           u = mfma_f32(s_inv[16 * mb + rl][16 * mb + 4 * kk + kg],
                        s_tmp[wave][4 * kk + kg][rl], u);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          s_inv[16 * mb + 4 * kg + i][16 * nb + rl] = -u[i];
+        for (int e = 0; e < 4; ++e) {
+          s_inv[16 * mb + 4 * kg + e][16 * nb + rl] = -u[e];
+          s_invb[16 * mb + 4 * kg + e][16 * nb + rl] = (bf16)(-u[e]);
+        }
       }
       __syncthreads();
     }
 
     // ---- 5. W = INV (beta k e^a) (row-major, via W^T tiles) and
     //         U~ = INV (beta v) (stored transposed) ------------------------
-    {
-      constexpr int KT = K / 16, VT = V / 16;
-      constexpr int NT = NSUB * (KT + VT);
-      for (int t = wave; t < NT; t += 4) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = wave * TPW + i;
+      if (t < NTILE) {
         const int m = t / (KT + VT), ct = t % (KT + VT);
         const bool isW = ct < KT;
         const int col = 16 * (isW ? ct : ct - KT) + rl;
@@ -376,10 +414,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a,
           const int s0 = 32 * cs + 8 * kg;
           bf16x8 iv = zero_bf16x8(), bv = zero_bf16x8();
           if (s0 < C) {
-            float x[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = s_inv[r][s0 + i];
-            iv = pack8(x);
+            iv = *reinterpret_cast<const bf16x8*>(&s_invb[r][s0]);
             bv = *reinterpret_cast<const bf16x8*>(isW ? &s_kbT[col][s0]
                                                       : &s_vbT[col][s0]);
           }
@@ -388,7 +423,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a,
         }
         bf16x4 ov;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = (bf16)acc[i];
+        for (int e = 0; e < 4; ++e) ov[e] = (bf16)acc[e];
         if (isW) {
           *reinterpret_cast<bf16x4*>(gW + r * K + 16 * ct + 4 * kg) = ov;
         } else {
@@ -410,13 +445,13 @@ hipError_t launch(const PrefillArgs& a, hipStream_t st) {
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void*>(prep_kernel<Tin, D, C>), 256, 0);
+        &per_cu, reinterpret_cast<const void*>(prep_kernel<Tin, D, C>), 512, 0);
   if (e != hipSuccess) return e;
   const int64_t resident = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
   const unsigned grid = (unsigned)(items < resident ? items : resident);
   void* args[] = {const_cast<PrefillArgs*>(&a), const_cast<int64_t*>(&items)};
   return hipLaunchKernel(reinterpret_cast<const void*>(prep_kernel<Tin, D, C>),
-                         dim3(grid), dim3(256), args, 0, st);
+                         dim3(grid), dim3(512), args, 0, st);
 }
 
 template <typename Tin, int D>
