@@ -39,6 +39,9 @@ kda_status_t run_prefill(kda::PrefillArgs& a, int32_t D, int32_t C,
   if (need == 0) return KDA_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
+  // the prep kernel indexes its (sequence, chunk, head) items in 32 bits
+  if ((int64_t)a.N * a.max_chunks * a.H >= ((int64_t)1 << 31))
+    return KDA_ERR_UNSUPPORTED;
   a.ws = static_cast<char*>(workspace);
   a.nslots = kda::num_slots(a.N, a.total_T, C);
   const bool bf16_io = dtype == KDA_DTYPE_BF16;

@@ -47,22 +47,35 @@ struct Item {
   bool valid;
 };
 
+template <bool kVarlen>
 __device__ __forceinline__ Item decode_item(const PrefillArgs& a, int C,
-                                            int64_t item) {
+                                            int64_t item64) {
+  // the host guarantees fewer than 2^31 items: 32-bit division is enough
+  const uint32_t item = (uint32_t)item64;
   Item it;
-  it.h = (int)(item % a.H);
-  const int64_t rest = item / a.H;
-  it.ci = (int)(rest % a.max_chunks);
-  it.n = (int)(rest / a.max_chunks);
+  it.h = (int)(item % (uint32_t)a.H);
+  const uint32_t rest = item / (uint32_t)a.H;
+  it.ci = (int)(rest % (uint32_t)a.max_chunks);
+  it.n = (int)(rest / (uint32_t)a.max_chunks);
   int64_t bos, eos;
-  seq_bounds(a, it.n, bos, eos);
+  if (kVarlen) {
+    seq_bounds(a, it.n, bos, eos);
+  } else {
+    bos = (int64_t)it.n * a.T_fixed;
+    eos = bos + a.T_fixed;
+  }
   it.t0 = bos + (int64_t)it.ci * C;
   it.valid = it.t0 < eos;
   it.L = it.valid ? ((eos - it.t0) < C ? (int)(eos - it.t0) : C) : 0;
   return it;
 }
 
-template <typename Tin, int D, int C>
+// kVarlen: items may lie past the end of their sequence (packed sequences
+// of different lengths).  Without it every item is valid and the loop body
+// has no branch around memory instructions, so the compiler can count the
+// outstanding loads and stores exactly and never has to drain the stores of
+// one item before using the prefetched inputs of the next.
+template <typename Tin, int D, int C, bool kVarlen>
 __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
                                                    int64_t total_items) {
   constexpr int NT = 512, NW = NT / 64;    // threads, waves
@@ -76,12 +89,13 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
   constexpr int PPT = (NPIECE + NT - 1) / NT;
   constexpr int NPAIR = NSUB * (NSUB + 1) / 2;  // (m, n <= m) tile pairs
   constexpr int NUP = NSUB * (NSUB - 1) / 2;    // (m, n > m): M is zero there
+  constexpr int NJOBW = (NPAIR + NUP + NW - 1) / NW;  // jobs per wave
   constexpr int KT = K / 16, VT = V / 16;
   constexpr int NTILE = NSUB * (KT + VT);  // W^T and U~ output tiles
   constexpr int TPW = (NTILE + NW - 1) / NW;
   constexpr int AP = K + 4, CP = C + 4, TP = C + 8, KP = K + 8;
   static_assert(NSUB >= 1 && NSUB <= 4 && C % TPC == 0 && K <= 512, "shape");
-  static_assert(NUP <= NW && NPAIR <= 2 * NW, "work split");
+  static_assert(NSUB * NSUB <= 2 * NW, "work split");
   // fp32 inputs at large head dims are staged as bf16 to fit LDS; every
   // product they feed takes bf16 operands anyway.
   using Lt = typename std::conditional<(sizeof(Tin) == 4 && D >= 64), bf16,
@@ -97,14 +111,20 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
   float (*s_a)[AP] = reinterpret_cast<float (*)[AP]>(s_abuf);
   float (*s_inv)[CP] = reinterpret_cast<float (*)[CP]>(s_abuf);
   __shared__ float s_A[C][CP];                                // beta-scaled A
-  __shared__ __attribute__((aligned(16))) Lt s_q[C][KP];      // q rows
   __shared__ __attribute__((aligned(16))) Lt s_k[C][KP];      // k rows
+  // row operands of A and M: k and q scaled by e^{a_r - rho_m(r)} (bf16)
+  __shared__ __attribute__((aligned(16))) bf16 s_kh[C][KP];
+  __shared__ __attribute__((aligned(16))) bf16 s_qh[C][KP];
   __shared__ __attribute__((aligned(16))) bf16 s_kbT[K][TP];  // (beta k e^a)^T
-  __shared__ __attribute__((aligned(16))) bf16 s_vbT[V][TP];  // (beta v)^T
+  // (beta v)^T, 8-element groups of s XOR-swizzled by row (vswz)
+  __shared__ __attribute__((aligned(16))) bf16 s_vbT[V][TP];
   __shared__ __attribute__((aligned(16))) bf16 s_invb[C][TP]; // INV, bf16
-  __shared__ float s_tmp[NW][16][20];
+  __shared__ float s_tmp[NSUB][16][20];
   __shared__ float s_beta[C];
   __shared__ float s_tot[TPC][K];
+  // column of element (j, s) of (beta v)^T: spreads the transposed 2-byte
+  // writes of one wave over more banks; 16-byte groups stay contiguous
+  auto vswz = [](int j, int s) { return s ^ (8 * ((j >> 3) & (C / 8 - 1))); };
 
   const int H = a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -144,7 +164,7 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
   float rg[RPT];
   Raw8<Tin> rq[PPT], rk[PPT], rv[PPT];
   float rbeta = 0.f;
-  auto load_inputs = [&](const Rs& R) {
+  auto load_gvb = [&](const Rs& R) {
     if (kFullScan || tid < SCAN_T) {
 #pragma unroll
       for (int i = 0; i < RPT; ++i)
@@ -156,37 +176,33 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
       const int p = tid + NT * i;
       if (kFullPieces || p < NPIECE) {
         const int pr = p / (K / 8), c0 = 8 * (p % (K / 8));
-        const uint32_t off =
-            (uint32_t)(((int64_t)pr * H * K + c0) * sizeof(Tin));
-        rq[i].load_buf(R.q, off);
-        rk[i].load_buf(R.k, off);
-        rv[i].load_buf(R.v, off);
+        rv[i].load_buf(R.v,
+                       (uint32_t)(((int64_t)pr * H * V + c0) * sizeof(Tin)));
       }
     }
     if (tid < C) rbeta = buffer_load_f32(R.b, (uint32_t)((int64_t)tid * H * 4));
   };
-
-  int64_t item = blockIdx.x;
-  bool have = false;  // prefetch registers hold `item`'s inputs
-  if (item < total_items) {
-    const Item it = decode_item(a, C, item);
-    if (it.valid) {
-      load_inputs(item_rsrc(it));
-      have = true;
+  auto load_qk = [&](const Rs& R) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int p = tid + NT * i;
+      if (kFullPieces || p < NPIECE) {
+        const int pr = p / (K / 8), c0 = 8 * (p % (K / 8));
+        const uint32_t off =
+            (uint32_t)(((int64_t)pr * H * K + c0) * sizeof(Tin));
+        rq[i].load_buf(R.q, off);
+        rk[i].load_buf(R.k, off);
+      }
     }
-  }
+  };
+  auto load_inputs = [&](const Rs& R) {
+    load_gvb(R);
+    load_qk(R);
+  };
 
-  for (; item < total_items; item += gridDim.x) {
-    const Item it = decode_item(a, C, item);
-    if (!it.valid) continue;  // uniform across the workgroup
-    if (!have) load_inputs(item_rsrc(it));
-    const int64_t next = item + gridDim.x;
-    Item nx;
-    nx.valid = false;
-    if (next < total_items) nx = decode_item(a, C, next);
-    have = nx.valid;
-    const Rs nrs = item_rsrc(nx.valid ? nx : it);  // harmless reload if none
-
+  // One item, with its inputs already in the prefetch registers; issues the
+  // prefetch of `nrs` as soon as the registers are free.
+  auto process = [&](const Item& it, const Rs& nrs) {
     const int h = it.h;
     const int64_t slot = it.t0 / C + it.n;
     char* blk = a.ws + ((size_t)h * a.nslots + slot) * lay.block_bytes;
@@ -217,8 +233,6 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
       if (kFullPieces || p < NPIECE) {
         const int pr = p / (K / 8), c0 = 8 * (p % (K / 8));
         float x[8];
-        rq[i].get(x);
-        lds_put8(&s_q[pr][c0], x);
         rk[i].get(x);
         lds_put8(&s_k[pr][c0], x);
       }
@@ -226,11 +240,11 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
     __syncthreads();
     if (kFullScan || tid < SCAN_T) {
       float off = 0.f;
-      for (int j = 0; j < sseg; ++j) off += s_tot[j][sc];
+#pragma unroll
+      for (int j = 0; j < TPC - 1; ++j)
+        if (j < sseg) off += s_tot[j][sc];
 #pragma unroll
       for (int i = 0; i < RPT; ++i) s_a[sseg * RPT + i][sc] = loc[i] + off;
-      if (sseg == TPC - 1)
-        gGamma[sc] = __builtin_amdgcn_exp2f(loc[RPT - 1] + off);
     }
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
@@ -241,26 +255,50 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
         rv[i].get(x);
         const float b = s_beta[pr];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s_vbT[c0 + e][pr] = (bf16)(b * x[e]);
+        for (int e = 0; e < 8; ++e)
+          s_vbT[c0 + e][vswz(c0 + e, pr)] = (bf16)(b * x[e]);
       }
     }
-    load_inputs(nrs);  // every prefetch register is free now
+    load_gvb(nrs);  // g, v, beta registers are free now
     __syncthreads();
 
-    // ---- 2. Q^ and K-bar^T (workspace), (beta k e^a)^T (LDS) -------------
+    // ---- 2. gamma, Q^ and K-bar^T (workspace), (beta k e^a)^T (LDS) ------
+    // gamma: every thread stores; threads past d_k fall outside the buffer.
+    __builtin_amdgcn_raw_buffer_store_b32(
+        __builtin_bit_cast(unsigned, __builtin_amdgcn_exp2f(s_a[C - 1][tid % K])),
+        make_rsrc(gGamma, K * 4), (uint32_t)(tid * 4), 0, 0);
+    // Q^ = q e^a (workspace) and the row operands k e^{a - rho}, q e^{a - rho}
+    // (LDS), rho = the decay just before the row's 16-row sub-tile.
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int p = tid + NT * i;
       if (kFullPieces || p < NPIECE) {
         const int pr = p / (K / 8), c0 = 8 * (p % (K / 8));
-        float x[8], av[8];
-        lds_get8(&s_q[pr][c0], x);
+        const int rb = pr & ~15;  // first row of the sub-tile
+        float x[8], kx[8], av[8], rho[8];
+        rq[i].get(x);
+        rk[i].get(kx);
         lds_get8(&s_a[pr][c0], av);
+        if (rb > 0) {
+          lds_get8(&s_a[rb - 1][c0], rho);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] *= __builtin_amdgcn_exp2f(av[e]);
-        *reinterpret_cast<bf16x8*>(gQh + pr * K + c0) = pack8(x);
+          for (int e = 0; e < 8; ++e) rho[e] = 0.f;
+        }
+        float qh[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = __builtin_amdgcn_exp2f(av[e] - rho[e]);
+          qh[e] = x[e] * __builtin_amdgcn_exp2f(av[e]);
+          x[e] *= f;
+          kx[e] *= f;
+        }
+        *reinterpret_cast<bf16x8*>(gQh + pr * K + c0) = pack8(qh);
+        *reinterpret_cast<bf16x8*>(&s_qh[pr][c0]) = pack8(x);
+        *reinterpret_cast<bf16x8*>(&s_kh[pr][c0]) = pack8(kx);
       }
     }
+    load_qk(nrs);  // q, k registers are free now
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int p = tid + NT * i;
@@ -280,27 +318,30 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
         *reinterpret_cast<bf16x8*>(&s_kbT[c][s0]) = pack8(kh);
       }
     }
+    __syncthreads();  // row operands complete
 
-    // ---- 3. A (LDS, fp32) and M (workspace, bf16): tile pairs (m, n <= m)
-    //         spread over the waves; zero tiles of M above the diagonal ----
+    // ---- 3. A (LDS, fp32) and M (workspace, bf16).  Jobs: the NPAIR tile
+    //         pairs (m, n <= m), then the NUP tiles of M above the diagonal
+    //         (zero); job j runs on wave j % NW, every job stores one tile of
+    //         M, and every wave runs the same number of jobs. ---------------
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int pidx = wave + NW * j;
-      if (pidx < NPAIR) {
+    for (int jj = 0; jj < NJOBW; ++jj) {
+      const int job = wave + NW * jj;
+      if (job < NPAIR) {
         int m = 0;
-        while ((m + 1) * (m + 2) / 2 <= pidx) ++m;
-        const int nn = pidx - m * (m + 1) / 2;
+        while ((m + 1) * (m + 2) / 2 <= job) ++m;
+        const int nn = job - m * (m + 1) / 2;
         const int r = 16 * m + rl, s = 16 * nn + rl;
         f32x4 accA = zero4(), accMT = zero4();
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
           const int c0 = 32 * ks + 8 * kg;
-          float kx[8], qx[8], kc[8];
+          bf16x8 kr = zero_bf16x8(), qr = zero_bf16x8();
+          float kc[8];
           if (kFullK || c0 < K) {
-            float ar[8], as[8], rho[8];
-            lds_get8(&s_k[r][c0], kx);
-            lds_get8(&s_q[r][c0], qx);
-            lds_get8(&s_a[r][c0], ar);
+            float as[8], rho[8];
+            kr = *reinterpret_cast<const bf16x8*>(&s_kh[r][c0]);
+            qr = *reinterpret_cast<const bf16x8*>(&s_qh[r][c0]);
             lds_get8(&s_k[s][c0], kc);
             lds_get8(&s_a[s][c0], as);
             if (m > 0) {
@@ -310,19 +351,15 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
               for (int e = 0; e < 8; ++e) rho[e] = 0.f;
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float f = __builtin_amdgcn_exp2f(ar[e] - rho[e]);
-              kx[e] *= f;
-              qx[e] *= f;
+            for (int e = 0; e < 8; ++e)
               kc[e] *= __builtin_amdgcn_exp2f(rho[e] - as[e]);
-            }
           } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) kx[e] = qx[e] = kc[e] = 0.f;
+            for (int e = 0; e < 8; ++e) kc[e] = 0.f;
           }
           const bf16x8 kcb = pack8(kc);
-          accA = mfma_bf16(pack8(kx), kcb, accA);    // A tile: rows r, cols s
-          accMT = mfma_bf16(kcb, pack8(qx), accMT);  // M^T tile: rows s, cols r
+          accA = mfma_bf16(kr, kcb, accA);    // A tile: rows r, cols s
+          accMT = mfma_bf16(kcb, qr, accMT);  // M^T tile: rows s, cols r
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -336,17 +373,16 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
           mv[e] = (bf16)(ss <= r ? accMT[e] : 0.f);
         }
         *reinterpret_cast<bf16x4*>(gM + r * C + 16 * nn + 4 * kg) = mv;
+      } else if (job < NPAIR + NUP) {
+        int z = job - NPAIR, m = 0;  // z-th tile above the diagonal
+        while (z >= NSUB - 1 - m) {
+          z -= NSUB - 1 - m;
+          ++m;
+        }
+        const int nn = m + 1 + z;
+        *reinterpret_cast<uint2*>(gM + (16 * m + rl) * C + 16 * nn + 4 * kg) =
+            make_uint2(0u, 0u);
       }
-    }
-    if (wave >= NW - NUP) {
-      int z = NW - 1 - wave, m = 0;  // z-th tile above the diagonal
-      while (z >= NSUB - 1 - m) {
-        z -= NSUB - 1 - m;
-        ++m;
-      }
-      const int nn = m + 1 + z;
-      *reinterpret_cast<uint2*>(gM + (16 * m + rl) * C + 16 * nn + 4 * kg) =
-          make_uint2(0u, 0u);
     }
     __syncthreads();  // A complete; the decay buffer is no longer read
 
@@ -402,8 +438,8 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
     //         U~ = INV (beta v) (stored transposed) ------------------------
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const int t = wave * TPW + i;
-      if (t < NTILE) {
+      const int t = wave + NW * i;  // interleaved: every wave sees every m
+      if (NTILE % NW == 0 || t < NTILE) {
         const int m = t / (KT + VT), ct = t % (KT + VT);
         const bool isW = ct < KT;
         const int col = 16 * (isW ? ct : ct - KT) + rl;
@@ -415,8 +451,8 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
           bf16x8 iv = zero_bf16x8(), bv = zero_bf16x8();
           if (s0 < C) {
             iv = *reinterpret_cast<const bf16x8*>(&s_invb[r][s0]);
-            bv = *reinterpret_cast<const bf16x8*>(isW ? &s_kbT[col][s0]
-                                                      : &s_vbT[col][s0]);
+            bv = *reinterpret_cast<const bf16x8*>(
+                isW ? &s_kbT[col][s0] : &s_vbT[col][vswz(col, s0)]);
           }
           acc = isW ? mfma_bf16(bv, iv, acc)   // W^T tile: rows c, cols r
                     : mfma_bf16(iv, bv, acc);  // U~ tile: rows r, cols j
@@ -431,13 +467,55 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
         }
       }
     }
+  };
+
+  int64_t item = blockIdx.x;
+  if (!kVarlen) {
+    // Every item is valid.  The first item is peeled so that both paths into
+    // the loop header have the same shape (prefetch loads, then one item's
+    // stores): the compiler then waits only for the loads it needs and never
+    // drains the previous item's stores.
+    if (item >= total_items) return;
+    Item it = decode_item<kVarlen>(a, C, item);
+    load_inputs(item_rsrc(it));
+    int64_t next = item + gridDim.x;
+    bool more = next < total_items;
+    Item nx = decode_item<kVarlen>(a, C, more ? next : item);
+    process(it, item_rsrc(nx));  // peeled; the last item reloads its inputs
+    while (more) {
+      item = next;
+      it = nx;
+      next = item + gridDim.x;
+      more = next < total_items;
+      nx = decode_item<kVarlen>(a, C, more ? next : item);
+      process(it, item_rsrc(nx));
+    }
+  } else {
+    bool have = false;  // prefetch registers hold `item`'s inputs
+    if (item < total_items) {
+      const Item it = decode_item<kVarlen>(a, C, item);
+      if (it.valid) {
+        load_inputs(item_rsrc(it));
+        have = true;
+      }
+    }
+    for (; item < total_items; item += gridDim.x) {
+      const Item it = decode_item<kVarlen>(a, C, item);
+      if (!it.valid) continue;  // uniform across the workgroup
+      if (!have) load_inputs(item_rsrc(it));
+      const int64_t next = item + gridDim.x;
+      const int64_t nclamp = next < total_items ? next : item;
+      const Item nx = decode_item<kVarlen>(a, C, nclamp);
+      have = next < total_items && nx.valid;
+      process(it, item_rsrc(nx.valid ? nx : it));
+    }
   }
 }
 
 // Persistent launch: as many workgroups as fit on the device at once, each
 // walking the work items with a stride of the grid size.
-template <typename Tin, int D, int C>
-hipError_t launch(const PrefillArgs& a, hipStream_t st) {
+template <typename Tin, int D, int C, bool kVarlen>
+hipError_t launch_v(const PrefillArgs& a, hipStream_t st) {
   const int64_t items = (int64_t)a.N * a.max_chunks * a.H;
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -445,13 +523,21 @@ hipError_t launch(const PrefillArgs& a, hipStream_t st) {
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void*>(prep_kernel<Tin, D, C>), 512, 0);
+        &per_cu, reinterpret_cast<const void*>(prep_kernel<Tin, D, C, kVarlen>),
+        512, 0);
   if (e != hipSuccess) return e;
   const int64_t resident = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
   const unsigned grid = (unsigned)(items < resident ? items : resident);
   void* args[] = {const_cast<PrefillArgs*>(&a), const_cast<int64_t*>(&items)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(prep_kernel<Tin, D, C>),
-                         dim3(grid), dim3(512), args, 0, st);
+  return hipLaunchKernel(
+      reinterpret_cast<const void*>(prep_kernel<Tin, D, C, kVarlen>),
+      dim3(grid), dim3(512), args, 0, st);
+}
+
+template <typename Tin, int D, int C>
+hipError_t launch(const PrefillArgs& a, hipStream_t st) {
+  return a.cu_seqlens ? launch_v<Tin, D, C, true>(a, st)
+                      : launch_v<Tin, D, C, false>(a, st);
 }
 
 template <typename Tin, int D>
