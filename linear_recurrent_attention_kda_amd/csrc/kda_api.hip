@@ -112,7 +112,7 @@ kda_status_t kda_prefill_chunked(const void* q, const void* k, const void* v,
   if ((initial_state && !aligned(initial_state, 16)) ||
       (final_state && !aligned(final_state, 16)))
     return KDA_ERR_INVALID_ARG;
-  if ((int64_t)(Dv / (Dv >= 32 ? 32 : 16)) * H * B > INT_MAX)
+  if ((int64_t)(Dv / 16) * H * B > INT_MAX)
     return KDA_ERR_UNSUPPORTED;
 
   kda::PrefillArgs a{};
@@ -150,7 +150,7 @@ kda_status_t kda_prefill_varlen(const void* q, const void* k, const void* v,
   if ((initial_state && !aligned(initial_state, 16)) ||
       (final_state && !aligned(final_state, 16)))
     return KDA_ERR_INVALID_ARG;
-  if ((int64_t)(Dv / (Dv >= 32 ? 32 : 16)) * H * N > INT_MAX)
+  if ((int64_t)(Dv / 16) * H * N > INT_MAX)
     return KDA_ERR_UNSUPPORTED;
   const int64_t maxlen = max_seqlen < total_T ? max_seqlen : total_T;
 

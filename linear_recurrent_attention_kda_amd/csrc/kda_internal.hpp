@@ -8,29 +8,52 @@
 namespace kda {
 
 // Per-(head, chunk slot) block of the prefill workspace, written by the
-// chunk-prep kernel and read by the chunk-recurrence kernel.  All bf16
-// except gamma:
-//   W    [C][Dk]   (I + A)^-1 diag(beta) Khat
-//   Qh   [C][Dk]   q * exp(a)
-//   KbT  [Dk][C]   (k * exp(a_last - a))^T
-//   UtT  [Dv][C]   ((I + A)^-1 diag(beta) v)^T
-//   M    [C][C]    decayed Q K^T, lower triangle incl. diagonal, zero above
-//   gamma[Dk] fp32 exp(a_last)
+// chunk-prep kernel and read by the chunk-recurrence kernel.  Every matrix is
+// stored fragment-major: the 16x32 bf16 MFMA operand fragment that a wave
+// reads with one 16-byte load per lane is 1 KB, stored contiguously in lane
+// order (lane l = row%16 + 16*((col%32)/8) holds row, cols 8*(l/16)..+7 of
+// its 32-column group), so each load instruction of the recurrence reads one
+// contiguous kilobyte.
+//   W    fragments (m, kk)  : rows of (I + A)^-1 diag(beta) Khat       [C x Dk]
+//   Qh   fragments (m, kk)  : q * exp(a)                              [C x Dk]
+//   KbT  fragments (ct, cs) : (k * exp(a_last - a))^T                 [Dk x C]
+//   M    fragments (m, cs)  : decayed Q K^T, lower incl. diag, 0 above [C x C]
+//   UtT  fragments (jt, m)  : ((I + A)^-1 diag(beta) v)^T, 8 bytes per lane
+//                             (row j = 16jt + l%16, cols 16m + 4(l/16)..+3)
+//   gamma[Dk] fp32          : exp(a_last)
+// m / ct / jt index 16-row tiles, kk / cs 32-column groups.  Fragment slots
+// of lanes past Dk or C (only when Dk or C is 16) are never read.
 struct WsLayout {
-  int C, Dk, Dv;
+  int C, Dk, Dv, kst, cst, mt;
   size_t off_W, off_Qh, off_KbT, off_UtT, off_M, off_gamma, block_bytes;
   __host__ __device__ static WsLayout make(int C, int Dk, int Dv) {
     WsLayout l;
     l.C = C; l.Dk = Dk; l.Dv = Dv;
+    l.kst = (Dk + 31) / 32;
+    l.cst = (C + 31) / 32;
+    l.mt = C / 16;
     size_t o = 0;
-    l.off_W = o;     o += (size_t)C * Dk * 2;
-    l.off_Qh = o;    o += (size_t)C * Dk * 2;
-    l.off_KbT = o;   o += (size_t)Dk * C * 2;
-    l.off_UtT = o;   o += (size_t)Dv * C * 2;
-    l.off_M = o;     o += (size_t)C * C * 2;
+    l.off_W = o;     o += (size_t)l.mt * l.kst * 1024;
+    l.off_Qh = o;    o += (size_t)l.mt * l.kst * 1024;
+    l.off_KbT = o;   o += (size_t)(Dk / 16) * l.cst * 1024;
+    l.off_UtT = o;   o += (size_t)(Dv / 16) * l.mt * 512;
+    l.off_M = o;     o += (size_t)l.mt * l.cst * 1024;
     l.off_gamma = o; o += (size_t)Dk * 4;
     l.block_bytes = (o + 255) / 256 * 256;
     return l;
+  }
+  // bf16 element offset of (row, col) inside a 16x32-fragment-major matrix
+  // whose column groups per 16-row tile number `groups`.
+  __host__ __device__ static size_t frag16(int row, int col, int groups) {
+    const int f = (row >> 4) * groups + (col >> 5);
+    const int lane = (row & 15) + 16 * ((col & 31) >> 3);
+    return ((size_t)f * 64 + lane) * 8 + (col & 7);
+  }
+  // bf16 element offset of U~^T (j, r) for the 8-byte-per-lane fragments.
+  __host__ __device__ static size_t frag_ut(int j, int r, int mt) {
+    const int f = (j >> 4) * mt + (r >> 4);
+    const int lane = (j & 15) + 16 * ((r & 15) >> 2);
+    return ((size_t)f * 64 + lane) * 4 + (r & 3);
   }
 };
 

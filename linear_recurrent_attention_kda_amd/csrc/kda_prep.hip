@@ -293,7 +293,8 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
           x[e] *= f;
           kx[e] *= f;
         }
-        *reinterpret_cast<bf16x8*>(gQh + pr * K + c0) = pack8(qh);
+        *reinterpret_cast<bf16x8*>(gQh + WsLayout::frag16(pr, c0, lay.kst)) =
+            pack8(qh);
         *reinterpret_cast<bf16x8*>(&s_qh[pr][c0]) = pack8(x);
         *reinterpret_cast<bf16x8*>(&s_kh[pr][c0]) = pack8(kx);
       }
@@ -314,7 +315,8 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
           kb[e] = kv * __builtin_amdgcn_exp2f(alast - as);
           kh[e] = s_beta[s] * kv * __builtin_amdgcn_exp2f(as);
         }
-        *reinterpret_cast<bf16x8*>(gKbT + c * C + s0) = pack8(kb);
+        *reinterpret_cast<bf16x8*>(gKbT + WsLayout::frag16(c, s0, lay.cst)) =
+            pack8(kb);
         *reinterpret_cast<bf16x8*>(&s_kbT[c][s0]) = pack8(kh);
       }
     }
@@ -372,7 +374,8 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
           const int ss = 16 * nn + 4 * kg + e;
           mv[e] = (bf16)(ss <= r ? accMT[e] : 0.f);
         }
-        *reinterpret_cast<bf16x4*>(gM + r * C + 16 * nn + 4 * kg) = mv;
+        *reinterpret_cast<bf16x4*>(
+            gM + WsLayout::frag16(r, 16 * nn + 4 * kg, lay.cst)) = mv;
       } else if (job < NPAIR + NUP) {
         int z = job - NPAIR, m = 0;  // z-th tile above the diagonal
         while (z >= NSUB - 1 - m) {
@@ -380,7 +383,8 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
           ++m;
         }
         const int nn = m + 1 + z;
-        *reinterpret_cast<uint2*>(gM + (16 * m + rl) * C + 16 * nn + 4 * kg) =
+        *reinterpret_cast<uint2*>(
+            gM + WsLayout::frag16(16 * m + rl, 16 * nn + 4 * kg, lay.cst)) =
             make_uint2(0u, 0u);
       }
     }
@@ -461,9 +465,11 @@ __global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
 #pragma unroll
         for (int e = 0; e < 4; ++e) ov[e] = (bf16)acc[e];
         if (isW) {
-          *reinterpret_cast<bf16x4*>(gW + r * K + 16 * ct + 4 * kg) = ov;
+          *reinterpret_cast<bf16x4*>(
+              gW + WsLayout::frag16(r, 16 * ct + 4 * kg, lay.kst)) = ov;
         } else {
-          *reinterpret_cast<bf16x4*>(gUtT + col * C + 16 * m + 4 * kg) = ov;
+          *reinterpret_cast<bf16x4*>(
+              gUtT + WsLayout::frag_ut(col, 16 * m + 4 * kg, lay.mt)) = ov;
         }
       }
     }

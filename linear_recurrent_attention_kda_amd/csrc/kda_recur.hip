@@ -21,6 +21,8 @@
 // MI355X consecutive workgroup ids go round-robin over the 8 XCDs (each with
 // its own L2); ids are remapped so that the slices of one head run on one
 // XCD and share its L2 copy of the head's chunk tensors.
+#include <stdlib.h>
+
 #include "kda_device.hpp"
 
 namespace kda {
@@ -39,7 +41,7 @@ struct ChunkOps {
   float4 gm[NCT];                 // gamma for the 4 state rows of the lane
 };
 
-template <typename Tout, int D, int C, int BV>
+template <typename Tout, int D, int C, int BV, int PF>
 __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
   constexpr int K = D, V = D;
   constexpr int NVT = V / BV;              // d_v slices per head
@@ -137,22 +139,23 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
       for (int kk = 0; kk < KSTEPS; ++kk) {
         const int c0 = 32 * kk + 8 * kg;
         if (kFullK || c0 < K) {
-          op.w[kk] = load_bf16x8(gW + (16 * mrow + rl) * K + c0);
-          op.qh[kk] = load_bf16x8(gQh + (16 * mrow + rl) * K + c0);
+          // fragment (mrow, kk), this lane's 16 bytes: one contiguous 1 KB
+          op.w[kk] = load_bf16x8(gW + ((mrow * lay.kst + kk) * 64 + lane) * 8);
+          op.qh[kk] = load_bf16x8(gQh + ((mrow * lay.kst + kk) * 64 + lane) * 8);
         }
       }
 #pragma unroll
       for (int cs = 0; cs < CSTEPS; ++cs) {
         const int s0 = 32 * cs + 8 * kg;   // M is zero above the diagonal
         if (kFullC || s0 < C)
-          op.m[cs] = load_bf16x8(gM + (16 * mrow + rl) * C + s0);
+          op.m[cs] = load_bf16x8(gM + ((mrow * lay.cst + cs) * 64 + lane) * 8);
       }
 #pragma unroll
       for (int i = 0; i < UPW; ++i) {
         const int jt = (u0 + i) % JT;
         if (kAllU || u0 + i < NUT)
           op.ut[i] = *reinterpret_cast<const uint2*>(
-              gUtT + (j0 + 16 * jt + rl) * C + 16 * mrow + 4 * kg);
+              gUtT + ((((j0 >> 4) + jt) * lay.mt + mrow) * 64 + lane) * 4);
       }
     }
     if (kAllS || has_s) {
@@ -163,7 +166,8 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
         for (int cs = 0; cs < CSTEPS; ++cs) {
           const int s0 = 32 * cs + 8 * kg;
           if (kFullC || s0 < C)
-            op.kb[lc][cs] = load_bf16x8(gKbT + (16 * ct + rl) * C + s0);
+            op.kb[lc][cs] =
+                load_bf16x8(gKbT + ((ct * lay.cst + cs) * 64 + lane) * 8);
         }
         op.gm[lc] = *reinterpret_cast<const float4*>(gG + 16 * ct + 4 * kg);
       }
@@ -260,39 +264,43 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
     }
   };
 
-  // Two register sets: chunk ci computes while chunk ci + 1 is in flight;
-  // the set freed by ci is refilled with ci + 2.
-  Ops opA, opB;
+  // PF register sets: chunk ci computes while chunks ci + 1 .. ci + PF - 1
+  // are in flight; the set freed by ci is refilled with ci + PF.
+  Ops ops[PF];
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) {
-    opA.w[kk] = opA.qh[kk] = opB.w[kk] = opB.qh[kk] = zero_bf16x8();
-  }
+  for (int f = 0; f < PF; ++f) {
 #pragma unroll
-  for (int cs = 0; cs < CSTEPS; ++cs) {
-    opA.m[cs] = opB.m[cs] = zero_bf16x8();
+    for (int kk = 0; kk < KSTEPS; ++kk) ops[f].w[kk] = ops[f].qh[kk] = zero_bf16x8();
 #pragma unroll
-    for (int lc = 0; lc < NCT; ++lc) opA.kb[lc][cs] = opB.kb[lc][cs] = zero_bf16x8();
-  }
+    for (int cs = 0; cs < CSTEPS; ++cs) {
+      ops[f].m[cs] = zero_bf16x8();
 #pragma unroll
-  for (int i = 0; i < UPW; ++i) opA.ut[i] = opB.ut[i] = make_uint2(0u, 0u);
-#pragma unroll
-  for (int lc = 0; lc < NCT; ++lc)
-    opA.gm[lc] = opB.gm[lc] = make_float4(0.f, 0.f, 0.f, 0.f);
-
-  // The pair loop has no branch in its body, so both paths into its header
-  // agree on the order of outstanding loads and the compiler waits only for
-  // the set it is about to use.
-  if (nchunks > 0) {
-    load_ops(opA, 0);
-    load_ops(opB, 1);
-    int64_t ci = 0;
-    for (; ci + 1 < nchunks; ci += 2) {
-      process(opA, ci);
-      load_ops(opA, ci + 2);
-      process(opB, ci + 1);
-      load_ops(opB, ci + 3);
+      for (int lc = 0; lc < NCT; ++lc) ops[f].kb[lc][cs] = zero_bf16x8();
     }
-    if (ci < nchunks) process(opA, ci);
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) ops[f].ut[i] = make_uint2(0u, 0u);
+#pragma unroll
+    for (int lc = 0; lc < NCT; ++lc)
+      ops[f].gm[lc] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+
+  // The loop body has no branch, so every path into its header agrees on
+  // the order of outstanding loads and the compiler waits only for the set
+  // it is about to use.
+  if (nchunks > 0) {
+#pragma unroll
+    for (int f = 0; f < PF; ++f) load_ops(ops[f], f);
+    int64_t ci = 0;
+    for (; ci + PF <= nchunks; ci += PF) {
+#pragma unroll
+      for (int f = 0; f < PF; ++f) {
+        process(ops[f], ci + f);
+        load_ops(ops[f], ci + f + PF);
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < PF - 1; ++f)
+      if (ci + f < nchunks) process(ops[f], ci + f);
   }
 
   if (a.final_state) {
@@ -310,12 +318,61 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
   }
 }
 
+template <typename Tout, int D, int C, int BV, int PF>
+hipError_t launch_bv(const PrefillArgs& a, hipStream_t st) {
+  const unsigned blocks = (unsigned)(D / BV) * (unsigned)a.H * (unsigned)a.N;
+  return launch_kernel(recur_kernel<Tout, D, C, BV, PF>, dim3(blocks),
+                       dim3(256), st, a);
+}
+
+// Slice width.  Wider slices re-read the per-chunk tensors fewer times and
+// do more matrix work per chunk loaded; narrower ones give more workgroups
+// when there are few (sequence, head) pairs.  Measured on MI355X: 96 heads
+// run fastest at 64 (192 workgroups), 32 heads at 16 (256 workgroups).
+// KDA_RECUR_BV (16 / 32 / 64) overrides the choice.
+inline int pick_bv(int D, int64_t units) {
+  static const int forced = [] {
+    const char* e = getenv("KDA_RECUR_BV");
+    return e ? atoi(e) : 0;
+  }();
+  int cus = 256;
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess)
+    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int bv = 16;
+  if (D >= 64 && units * (D / 64) >= cus / 2)
+    bv = 64;
+  else if (D >= 32 && units * (D / 32) >= cus)
+    bv = 32;
+  if ((forced == 16 || forced == 32 || forced == 64) && forced <= D) bv = forced;
+  return D == 16 ? 16 : bv;
+}
+
+// Register operand sets in flight (2 or 3); KDA_RECUR_PF overrides.
+inline int pick_pf() {
+  static const int forced = [] {
+    const char* e = getenv("KDA_RECUR_PF");
+    return e ? atoi(e) : 0;
+  }();
+  return forced == 3 ? 3 : 2;  // a third operand set measured no faster
+}
+
 template <typename Tout, int D, int C>
 hipError_t launch(const PrefillArgs& a, hipStream_t st) {
-  constexpr int BV = D >= 32 ? 32 : 16;
-  const unsigned blocks = (unsigned)(D / BV) * (unsigned)a.H * (unsigned)a.N;
-  return launch_kernel(recur_kernel<Tout, D, C, BV>, dim3(blocks), dim3(256),
-                       st, a);
+  const int bv = pick_bv(D, (int64_t)a.N * a.H);
+  const int pf = pick_pf();
+  if constexpr (D >= 64) {
+    if (bv == 64)
+      return pf == 2 ? launch_bv<Tout, D, C, 64, 2>(a, st)
+                     : launch_bv<Tout, D, C, 64, 3>(a, st);
+  }
+  if constexpr (D >= 32) {
+    if (bv == 32)
+      return pf == 2 ? launch_bv<Tout, D, C, 32, 2>(a, st)
+                     : launch_bv<Tout, D, C, 32, 3>(a, st);
+  }
+  return pf == 2 ? launch_bv<Tout, D, C, 16, 2>(a, st)
+                 : launch_bv<Tout, D, C, 16, 3>(a, st);
 }
 
 template <typename Tout, int D>
