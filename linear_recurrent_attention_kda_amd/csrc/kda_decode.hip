@@ -15,33 +15,45 @@
 // Mapping: one workgroup per (sequence, head).  Thread (rg, cg) owns the
 // float4 column group cg of rows rg, rg + RG, rg + 2 RG, ...; a wave reads
 // and writes whole contiguous rows (fully coalesced 16-byte accesses), the
-// slice stays in registers between the reduction and the write-back.
+// slice stays in registers between the reduction and the write-back.  The
+// state is touched exactly once per step, so its loads and stores may carry
+// the non-temporal cache policy (kNt) to keep it from displacing other data
+// in the caches.
+#include <stdlib.h>
+
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
 namespace kda {
 namespace {
 
-template <typename Tio, int D, int NT>
-__global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
+template <typename Tio, int D, int NT, bool kNt>
+__global__ __launch_bounds__(NT, (NT >= 1024 && sizeof(Tio) == 2) ? 8 : 1)
+void decode_kernel(DecodeArgs a) {
   constexpr int CG = D / 4;       // float4 column groups
   constexpr int RG = NT / CG;     // row groups
   constexpr int RPT = D / RG;     // rows per thread
+  constexpr int NW = NT / 64;     // waves
   static_assert(NT % CG == 0 && D % RG == 0, "decode tiling");
+  // a wave holds 64 / CG lanes of each column group (CG divides 32)
+  static_assert(32 % CG == 0 && NT >= 64, "decode lane grouping");
 
   __shared__ float s_alpha[D], s_k[D], s_q[D];
-  __shared__ float4 s_red[RG][CG][3];
+  __shared__ float4 s_red[NW][CG][3];
 
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
   const int cg = tid % CG, rg = tid / CG;
   float* S = a.state + (size_t)bh * D * D;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, D * D * 4);
+  constexpr int kPol = kNt ? kCachePolicyNt : 0;
 
   float4 s[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
-    s[i] = *reinterpret_cast<const float4*>(S + (size_t)(rg + RG * i) * D +
-                                            4 * cg);
+    s[i] = __builtin_bit_cast(
+        float4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, ((rg + RG * i) * D + 4 * cg) * 4, 0, kPol));
 
   const Tio* q = static_cast<const Tio*>(a.q) + (size_t)bh * D;
   const Tio* k = static_cast<const Tio*>(a.k) + (size_t)bh * D;
@@ -52,28 +64,42 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-  float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+  // per-thread partial sums over its rows, then over the lanes of the wave
+  // with the same column group (shuffles), then over the waves (LDS)
+  float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
   float qk = 0.f;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int c = rg + RG * i;
     const float al = s_alpha[c], kc = s_k[c], qc = s_q[c];
     s[i].x *= al; s[i].y *= al; s[i].z *= al; s[i].w *= al;
-    x.x += s[i].x * kc; x.y += s[i].y * kc; x.z += s[i].z * kc; x.w += s[i].w * kc;
-    y.x += s[i].x * qc; y.y += s[i].y * qc; y.z += s[i].z * qc; y.w += s[i].w * qc;
+    x[0] += s[i].x * kc; x[1] += s[i].y * kc; x[2] += s[i].z * kc; x[3] += s[i].w * kc;
+    y[0] += s[i].x * qc; y[1] += s[i].y * qc; y[2] += s[i].z * qc; y[3] += s[i].w * qc;
     qk += qc * kc;
   }
-  s_red[rg][cg][0] = x;
-  s_red[rg][cg][1] = y;
-  s_red[rg][cg][2] = make_float4(qk, 0.f, 0.f, 0.f);
+  // lanes l and l ^ off share a column group for every off in CG..32
+#pragma unroll
+  for (int off = 32; off >= CG; off >>= 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] += __shfl_xor(x[j], off);
+      y[j] += __shfl_xor(y[j], off);
+    }
+    qk += __shfl_xor(qk, off);
+  }
+  if ((tid & 63) < CG) {
+    const int w = tid / 64;
+    s_red[w][cg][0] = make_float4(x[0], x[1], x[2], x[3]);
+    s_red[w][cg][1] = make_float4(y[0], y[1], y[2], y[3]);
+    s_red[w][cg][2] = make_float4(qk, 0.f, 0.f, 0.f);
+  }
   __syncthreads();
 
   float4 X = make_float4(0.f, 0.f, 0.f, 0.f);
   float4 Y = make_float4(0.f, 0.f, 0.f, 0.f);
   float QK = 0.f;
 #pragma unroll
-  for (int r = 0; r < RG; ++r) {
+  for (int r = 0; r < NW; ++r) {
     const float4 xr = s_red[r][cg][0], yr = s_red[r][cg][1];
     X.x += xr.x; X.y += xr.y; X.z += xr.z; X.w += xr.w;
     Y.x += yr.x; Y.y += yr.y; Y.z += yr.z; Y.w += yr.w;
@@ -103,16 +129,53 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     float4 w;
     w.x = s[i].x + kc * u.x; w.y = s[i].y + kc * u.y;
     w.z = s[i].z + kc * u.z; w.w = s[i].w + kc * u.w;
-    *reinterpret_cast<float4*>(S + (size_t)c * D + 4 * cg) = w;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), rs,
+                                           (c * D + 4 * cg) * 4, 0, kPol);
   }
+}
+
+// Launch shape: threads per workgroup (capped by D^2 / 4, one float4 per
+// thread and row group) and the cache policy of the state accesses.  At
+// D = 128, 1024 threads hold 4 rows each in 60 VGPRs, so two workgroups
+// (128 KB of state loads) are in flight per CU.
+// KDA_DECODE_THREADS (256, 512, 1024) and KDA_DECODE_NT (0, 1) override the
+// defaults for tuning sweeps.
+struct DecodeShape {
+  int threads;
+  bool nt;
+};
+
+DecodeShape decode_shape() {
+  static const DecodeShape shape = [] {
+    DecodeShape d{1024, true};
+    if (const char* e = getenv("KDA_DECODE_THREADS")) {
+      const int t = atoi(e);
+      if (t == 256 || t == 512 || t == 1024) d.threads = t;
+    }
+    if (const char* e = getenv("KDA_DECODE_NT")) d.nt = atoi(e) != 0;
+    return d;
+  }();
+  return shape;
+}
+
+template <typename Tio, int D, int NT>
+hipError_t launch_nt(const DecodeArgs& a, bool nt, hipStream_t st) {
+  constexpr int T = (D * D / 4) < NT ? (D * D / 4) : NT;
+  const unsigned blocks = (unsigned)a.B * (unsigned)a.H;
+  return nt ? launch_kernel(decode_kernel<Tio, D, T, true>, dim3(blocks),
+                            dim3(T), st, a)
+            : launch_kernel(decode_kernel<Tio, D, T, false>, dim3(blocks),
+                            dim3(T), st, a);
 }
 
 template <typename Tio, int D>
 hipError_t launch(const DecodeArgs& a, hipStream_t st) {
-  constexpr int NT = (D * D / 4) < 256 ? (D * D / 4) : 256;
-  const unsigned blocks = (unsigned)a.B * (unsigned)a.H;
-  return launch_kernel(decode_kernel<Tio, D, NT>, dim3(blocks), dim3(NT), st,
-                       a);
+  const DecodeShape sh = decode_shape();
+  switch (sh.threads) {
+    case 512: return launch_nt<Tio, D, 512>(a, sh.nt, st);
+    case 1024: return launch_nt<Tio, D, 1024>(a, sh.nt, st);
+  }
+  return launch_nt<Tio, D, 256>(a, sh.nt, st);
 }
 
 template <typename Tio>

@@ -151,6 +151,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes,
                                            0x00020000);
 }
+// Cache-policy operand of the buffer intrinsics on gfx950: the "nt"
+// (non-temporal, streaming) bit.
+constexpr int kCachePolicyNt = 2;
 // Raw buffer loads (out-of-range -> 0).
 __device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r,
                                                  uint32_t off) {

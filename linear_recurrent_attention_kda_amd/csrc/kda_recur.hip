@@ -41,16 +41,16 @@ struct ChunkOps {
   float4 gm[NCT];                 // gamma for the 4 state rows of the lane
 };
 
-template <typename Tout, int D, int C, int BV, int PF>
-__global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
+template <typename Tout, int D, int C, int BV, int PF, int NW>
+__global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
   constexpr int K = D, V = D;
   constexpr int NVT = V / BV;              // d_v slices per head
   constexpr int KT = K / 16, JT = BV / 16; // 16x16 tiles of the slice
   constexpr int NST = KT * JT;             // state tiles
-  constexpr int SPW = (NST + 3) / 4;       // state tiles per wave
+  constexpr int SPW = (NST + NW - 1) / NW; // state tiles per wave
   constexpr int MT = C / 16;               // 16-row tiles of a chunk
   constexpr int NUT = MT * JT;             // U / O tiles per chunk
-  constexpr int UPW = (NUT + 3) / 4;       // U / O tiles per wave
+  constexpr int UPW = (NUT + NW - 1) / NW; // U / O tiles per wave
   constexpr int NCT = SPW >= JT ? SPW / JT : 1;  // state row tiles per wave
   constexpr int KSTEPS = (K + 31) / 32;
   constexpr int CSTEPS = (C + 31) / 32;
@@ -93,8 +93,8 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
   // for all of them, which would serialise the prefetch).
   constexpr bool kFullK = K % 32 == 0;      // every lane's column group < K
   constexpr bool kFullC = C % 32 == 0;      // every lane's row group < C
-  constexpr bool kAllU = NUT % 4 == 0;      // every wave owns U/O tiles
-  constexpr bool kAllS = NST % 4 == 0;      // every wave owns state tiles
+  constexpr bool kAllU = NUT % NW == 0;     // every wave owns U/O tiles
+  constexpr bool kAllS = NST % NW == 0;     // every wave owns state tiles
 
   // ---- initial state -> accumulators (D layout: row c = 16ct + 4kg + e,
   //      column j = 16jt + rl) and its bf16 copy -----------------------------
@@ -318,11 +318,11 @@ __global__ __launch_bounds__(256) void recur_kernel(PrefillArgs a) {
   }
 }
 
-template <typename Tout, int D, int C, int BV, int PF>
+template <typename Tout, int D, int C, int BV, int PF, int NW>
 hipError_t launch_bv(const PrefillArgs& a, hipStream_t st) {
   const unsigned blocks = (unsigned)(D / BV) * (unsigned)a.H * (unsigned)a.N;
-  return launch_kernel(recur_kernel<Tout, D, C, BV, PF>, dim3(blocks),
-                       dim3(256), st, a);
+  return launch_kernel(recur_kernel<Tout, D, C, BV, PF, NW>, dim3(blocks),
+                       dim3(64 * NW), st, a);
 }
 
 // Slice width.  Wider slices re-read the per-chunk tensors fewer times and
@@ -357,22 +357,35 @@ inline int pick_pf() {
   return forced == 3 ? 3 : 2;  // a third operand set measured no faster
 }
 
+// Waves per workgroup (4 or 8); KDA_RECUR_WAVES overrides.
+inline int pick_waves() {
+  static const int forced = [] {
+    const char* e = getenv("KDA_RECUR_WAVES");
+    return e ? atoi(e) : 0;
+  }();
+  return forced == 8 ? 8 : 4;
+}
+
+template <typename Tout, int D, int C, int BV>
+hipError_t launch_w(const PrefillArgs& a, hipStream_t st) {
+  const int pf = pick_pf();
+  if (pick_waves() == 8 && (D / 16) * (BV / 16) >= 8 && (C / 16) * (BV / 16) >= 8)
+    return pf == 2 ? launch_bv<Tout, D, C, BV, 2, 8>(a, st)
+                   : launch_bv<Tout, D, C, BV, 3, 8>(a, st);
+  return pf == 2 ? launch_bv<Tout, D, C, BV, 2, 4>(a, st)
+                 : launch_bv<Tout, D, C, BV, 3, 4>(a, st);
+}
+
 template <typename Tout, int D, int C>
 hipError_t launch(const PrefillArgs& a, hipStream_t st) {
   const int bv = pick_bv(D, (int64_t)a.N * a.H);
-  const int pf = pick_pf();
   if constexpr (D >= 64) {
-    if (bv == 64)
-      return pf == 2 ? launch_bv<Tout, D, C, 64, 2>(a, st)
-                     : launch_bv<Tout, D, C, 64, 3>(a, st);
+    if (bv == 64) return launch_w<Tout, D, C, 64>(a, st);
   }
   if constexpr (D >= 32) {
-    if (bv == 32)
-      return pf == 2 ? launch_bv<Tout, D, C, 32, 2>(a, st)
-                     : launch_bv<Tout, D, C, 32, 3>(a, st);
+    if (bv == 32) return launch_w<Tout, D, C, 32>(a, st);
   }
-  return pf == 2 ? launch_bv<Tout, D, C, 16, 2>(a, st)
-                 : launch_bv<Tout, D, C, 16, 3>(a, st);
+  return launch_w<Tout, D, C, 16>(a, st);
 }
 
 template <typename Tout, int D>
