@@ -20,17 +20,27 @@
 // Decay numerics ("Two Paths: Kimi K3 vs DeepSeek V4 Architecture
 // Divergence", section "Hardware Adaptation"): with log-decay >= -5, 16
 // consecutive tokens decay by at most e^-80, whose reciprocal is still a
-// normal bf16 number.  A and M are therefore formed per 16-row sub-tile m
-// (first row b_m) with the reference rho_m = a_{b_m - 1}:
-//   e^{a_r - a_s} = e^{a_r - rho_m} * e^{rho_m - a_s},
-// the row factor in [e^-80, 1], the column factor in [1, e^80] on the
-// diagonal sub-tile and <= 1 to its left, and both operands go to the bf16
-// matrix cores.  Exponents are kept in log2 units and evaluated with exp2.
+// normal bf16 number.  A and M are therefore formed per 16-row sub-tile pair
+// (m, n <= m), rho_j = a_{16j - 1} (rho_0 = 0) being the decay at the end of
+// sub-tile j - 1:
+//   e^{a_r - a_s} = e^{a_r - rho_m} * e^{rho_m - rho_{n+1}} * e^{rho_{n+1} - a_s}
+// The row operand k_r e^{a_r - rho_m} and the column base k_s e^{rho_{n+1} -
+// a_s} lie in [e^-80, 1] times k; the per-channel factor e^{rho_m -
+// rho_{n+1}} is <= 1 off the diagonal and in [1, e^80] on it, and it is
+// applied to the column base just before the product, so every bf16 matrix
+// core operand stays a normal number (a factor that underflows drops only
+// terms below the smallest normal fp32 number).  Exponents are kept in log2 units and evaluated with
+// exp2.
 //
-// gfx950 mapping: 256 threads (4 waves) per (chunk, head); wave m owns
-// 16-row sub-tile m.  Products use v_mfma_f32_16x16x32_bf16 (A, M, W, U~)
-// and v_mfma_f32_16x16x4_f32 (the off-diagonal blocks of INV).  Outputs are
-// written in the layouts the recurrence kernel reads as MFMA operands.
+// gfx950 mapping: one 256-thread workgroup (4 waves) per (chunk, head) and
+// under 80 KB of LDS, so that two chunks share a CU and one's barriers and
+// memory waits overlap the other's work.  Thread (channel group cg, row
+// group) loads 8 channels of RPT consecutive rows with 16-byte accesses,
+// scans the decay in registers (shuffles inside a wave, LDS across waves),
+// and forms every exponentiated operand from registers.  Products use
+// v_mfma_f32_16x16x32_bf16 (A, M, W, U~) and v_mfma_f32_16x16x4_f32 (the
+// off-diagonal blocks of INV).  Outputs are written in the layouts the
+// recurrence kernel reads as MFMA operands.
 #include <type_traits>
 
 #include "kda_device.hpp"
@@ -47,503 +57,435 @@ struct Item {
   bool valid;
 };
 
-template <bool kVarlen>
 __device__ __forceinline__ Item decode_item(const PrefillArgs& a, int C,
-                                            int64_t item64) {
+                                            uint32_t item) {
   // the host guarantees fewer than 2^31 items: 32-bit division is enough
-  const uint32_t item = (uint32_t)item64;
   Item it;
   it.h = (int)(item % (uint32_t)a.H);
   const uint32_t rest = item / (uint32_t)a.H;
   it.ci = (int)(rest % (uint32_t)a.max_chunks);
   it.n = (int)(rest / (uint32_t)a.max_chunks);
   int64_t bos, eos;
-  if (kVarlen) {
-    seq_bounds(a, it.n, bos, eos);
-  } else {
-    bos = (int64_t)it.n * a.T_fixed;
-    eos = bos + a.T_fixed;
-  }
+  seq_bounds(a, it.n, bos, eos);
   it.t0 = bos + (int64_t)it.ci * C;
   it.valid = it.t0 < eos;
   it.L = it.valid ? ((eos - it.t0) < C ? (int)(eos - it.t0) : C) : 0;
   return it;
 }
 
-// kVarlen: items may lie past the end of their sequence (packed sequences
-// of different lengths).  Without it every item is valid and the loop body
-// has no branch around memory instructions, so the compiler can count the
-// outstanding loads and stores exactly and never has to drain the stores of
-// one item before using the prefetched inputs of the next.
-template <typename Tin, int D, int C, bool kVarlen>
-__global__ __launch_bounds__(512) void prep_kernel(PrefillArgs a,
-                                                   int64_t total_items) {
-  constexpr int NT = 512, NW = NT / 64;    // threads, waves
+// n consecutive bf16 values (n = 1, 2 or 4) at p.
+template <int N>
+__device__ __forceinline__ void store_bf16xn(bf16* p, const float (&x)[N]) {
+  if constexpr (N == 4) {
+    bf16x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (bf16)x[i];
+    *reinterpret_cast<bf16x4*>(p) = v;
+  } else if constexpr (N == 2) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v;
+    v[0] = (bf16)x[0];
+    v[1] = (bf16)x[1];
+    *reinterpret_cast<bf16x2*>(p) = v;
+  } else {
+    static_assert(N == 1, "1, 2 or 4 values");
+    *p = (bf16)x[0];
+  }
+}
+
+template <typename Tin, int D, int C>
+__global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
+  constexpr int NT = 256, NW = NT / kWave;  // threads, waves
   constexpr int K = D, V = D;
-  constexpr int NSUB = C / 16;             // 16-row sub-tiles per chunk
-  constexpr int KSTEPS = (K + 31) / 32;    // 32-wide column groups of a row
-  constexpr int TPC = (NT / K) < C ? (NT / K) : C;  // scan threads / channel
-  constexpr int RPT = C / TPC;             // rows per scan thread
-  constexpr int SCAN_T = TPC * K;          // threads taking part in the scan
-  constexpr int NPIECE = C * K / 8;        // 8-element pieces of q, k, v
-  constexpr int PPT = (NPIECE + NT - 1) / NT;
+  constexpr int NSUB = C / 16;              // 16-row sub-tiles per chunk
+  constexpr int CGN = D / 8;                // 8-channel groups of a row
+  constexpr int RPT = (C * CGN) / NT > 0 ? (C * CGN) / NT : 1;  // rows/thread
+  constexpr int NST = (C / RPT) * CGN;      // staging threads
+  constexpr int KSTEPS = (K + 31) / 32;     // 32-wide channel groups of a row
   constexpr int NPAIR = NSUB * (NSUB + 1) / 2;  // (m, n <= m) tile pairs
   constexpr int NUP = NSUB * (NSUB - 1) / 2;    // (m, n > m): M is zero there
   constexpr int NJOBW = (NPAIR + NUP + NW - 1) / NW;  // jobs per wave
   constexpr int KT = K / 16, VT = V / 16;
   constexpr int NTILE = NSUB * (KT + VT);  // W^T and U~ output tiles
   constexpr int TPW = (NTILE + NW - 1) / NW;
-  constexpr int AP = K + 4, CP = C + 4, TP = C + 8, KP = K + 8;
-  static_assert(NSUB >= 1 && NSUB <= 4 && C % TPC == 0 && K <= 512, "shape");
-  static_assert(NSUB * NSUB <= 2 * NW, "work split");
-  // fp32 inputs at large head dims are staged as bf16 to fit LDS; every
-  // product they feed takes bf16 operands anyway.
-  using Lt = typename std::conditional<(sizeof(Tin) == 4 && D >= 64), bf16,
-                                       Tin>::type;
-  constexpr bool kFullScan = SCAN_T == NT;
-  constexpr bool kFullPieces = NPIECE % NT == 0;
+  constexpr int RP = D + 8;  // bf16 row stride of the [C][D] row operands
+  constexpr int TP = C + 8;  // bf16 row stride of the [D][C] transposes
+  constexpr int AP = C + 4;  // fp32 row stride of A and INV
+  static_assert(NSUB >= 1 && NSUB <= 4 && CGN <= kWave, "shape");
+  static_assert(NST <= NT && 8 % RPT == 0, "staging split");
+  static_assert(C * TP * 2 <= C * AP * 4, "INV (bf16) fits in A's storage");
+  constexpr bool kFullSt = NST == NT;
   constexpr bool kFullK = K % 32 == 0;
 
-  // s_a (cumulative log2-decay) is dead once A and M are formed; the
-  // inverse then reuses its storage.
-  constexpr int ABUF = C * (AP > CP ? AP : CP);
-  __shared__ __attribute__((aligned(16))) float s_abuf[ABUF];
-  float (*s_a)[AP] = reinterpret_cast<float (*)[AP]>(s_abuf);
-  float (*s_inv)[CP] = reinterpret_cast<float (*)[CP]>(s_abuf);
-  __shared__ float s_A[C][CP];                                // beta-scaled A
-  __shared__ __attribute__((aligned(16))) Lt s_k[C][KP];      // k rows
-  // row operands of A and M: k and q scaled by e^{a_r - rho_m(r)} (bf16)
-  __shared__ __attribute__((aligned(16))) bf16 s_kh[C][KP];
-  __shared__ __attribute__((aligned(16))) bf16 s_qh[C][KP];
-  __shared__ __attribute__((aligned(16))) bf16 s_kbT[K][TP];  // (beta k e^a)^T
-  // (beta v)^T, 8-element groups of s XOR-swizzled by row (vswz)
-  __shared__ __attribute__((aligned(16))) bf16 s_vbT[V][TP];
-  __shared__ __attribute__((aligned(16))) bf16 s_invb[C][TP]; // INV, bf16
-  __shared__ float s_tmp[NSUB][16][20];
+  // LDS.  Region R is reused across phases:
+  //   scan:        wave totals [NW][D] fp32
+  //   stages 1-3:  qh, kh, kcb [C][RP] bf16 (row operands, column base)
+  //   stages 4-5:  kbT, vbT [D][TP] bf16, INV [C][AP] fp32, tmp [NSUB][16][20]
+  constexpr int R_OPS = 3 * C * RP * 2;
+  constexpr int R_KB = 0, R_VB = D * TP * 2, R_INV = 2 * D * TP * 2;
+  constexpr int R_TMP = R_INV + C * AP * 4;
+  constexpr int R_LATE = R_TMP + NSUB * 16 * 20 * 4;
+  constexpr int R_BYTES = R_OPS > R_LATE ? (R_OPS > NW * D * 4 ? R_OPS : NW * D * 4)
+                                         : (R_LATE > NW * D * 4 ? R_LATE : NW * D * 4);
+  __shared__ __attribute__((aligned(16))) char s_r[R_BYTES];
+  __shared__ __attribute__((aligned(16))) float s_A[C][AP];  // later INV bf16
+  __shared__ __attribute__((aligned(16))) float s_rho[NSUB + 1][D];
   __shared__ float s_beta[C];
-  __shared__ float s_tot[TPC][K];
-  // column of element (j, s) of (beta v)^T: spreads the transposed 2-byte
-  // writes of one wave over more banks; 16-byte groups stay contiguous
-  auto vswz = [](int j, int s) { return s ^ (8 * ((j >> 3) & (C / 8 - 1))); };
+  float (*s_wtot)[D] = reinterpret_cast<float (*)[D]>(s_r);
+  bf16 (*s_qh)[RP] = reinterpret_cast<bf16 (*)[RP]>(s_r);
+  bf16 (*s_kh)[RP] = reinterpret_cast<bf16 (*)[RP]>(s_r + C * RP * 2);
+  bf16 (*s_kcb)[RP] = reinterpret_cast<bf16 (*)[RP]>(s_r + 2 * C * RP * 2);
+  bf16 (*s_kbT)[TP] = reinterpret_cast<bf16 (*)[TP]>(s_r + R_KB);
+  bf16 (*s_vbT)[TP] = reinterpret_cast<bf16 (*)[TP]>(s_r + R_VB);
+  float (*s_inv)[AP] = reinterpret_cast<float (*)[AP]>(s_r + R_INV);
+  float (*s_tmp)[16][20] = reinterpret_cast<float (*)[16][20]>(s_r + R_TMP);
+  bf16 (*s_invb)[TP] = reinterpret_cast<bf16 (*)[TP]>(&s_A[0][0]);
+  // column of element (c, s) of the transposes: 16-byte groups of s
+  // XOR-swizzled by channel so that one wave's writes spread over the banks
+  auto swz = [](int c, int s) { return s ^ (8 * ((c >> 3) & (C / 8 - 1))); };
+
+  const Item it = decode_item(a, C, blockIdx.x);
+  if (!it.valid) return;  // past the end of a packed sequence (uniform)
 
   const int H = a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rl = lane & 15, kg = lane >> 4;
-  const int sc = tid % K, sseg = tid / K;  // scan layout
-  const Tin* qg = static_cast<const Tin*>(a.q);
-  const Tin* kgp = static_cast<const Tin*>(a.k);
-  const Tin* vg = static_cast<const Tin*>(a.v);
+  const int cg = tid % CGN, r0 = (tid / CGN) * RPT, c0 = 8 * cg;
+  const bool active = kFullSt || tid < NST;
   const WsLayout lay = WsLayout::make(C, K, V);
 
-  // Blocks of INV above the diagonal are never written: zero their bf16
-  // copy once.
-  for (int e = tid; e < C * C; e += NT) {
-    const int r = e / C, c = e % C;
-    if (c / 16 > r / 16) s_invb[r][c] = (bf16)0.f;
-  }
+  const int h = it.h;
+  const int64_t slot = it.t0 / C + it.n;
+  char* blk = a.ws + ((size_t)h * a.nslots + slot) * lay.block_bytes;
+  bf16* gW = reinterpret_cast<bf16*>(blk + lay.off_W);
+  bf16* gQh = reinterpret_cast<bf16*>(blk + lay.off_Qh);
+  bf16* gKbT = reinterpret_cast<bf16*>(blk + lay.off_KbT);
+  bf16* gUtT = reinterpret_cast<bf16*>(blk + lay.off_UtT);
+  bf16* gM = reinterpret_cast<bf16*>(blk + lay.off_M);
+  float* gGamma = reinterpret_cast<float*>(blk + lay.off_gamma);
 
-  // Input buffers of one item: rows t0 .. t0+L-1 of (token, head); rows past
-  // L fall outside the buffer and load as 0.
-  struct Rs {
-    __amdgpu_buffer_rsrc_t q, k, v, g, b;
-  };
-  auto item_rsrc = [&](const Item& it) {
-    Rs r;
-    const int64_t row0 = it.t0 * H + it.h;
-    const int64_t span = (int64_t)(it.L - 1) * H;
-    r.q = make_rsrc(qg + row0 * K, (uint32_t)((span * K + K) * sizeof(Tin)));
-    r.k = make_rsrc(kgp + row0 * K, (uint32_t)((span * K + K) * sizeof(Tin)));
-    r.v = make_rsrc(vg + row0 * V, (uint32_t)((span * V + V) * sizeof(Tin)));
-    r.g = make_rsrc(a.g + row0 * K, (uint32_t)((span * K + K) * 4));
-    r.b = make_rsrc(a.beta + row0, (uint32_t)((span + 1) * 4));
-    return r;
-  };
+  // ---- 0. inputs: rows t0 .. t0+L-1 of (token, head); rows past L fall
+  //         outside the buffers and load as 0 --------------------------------
+  const int64_t row0 = it.t0 * H + h;
+  const int64_t span = (int64_t)(it.L - 1) * H;
+  const __amdgpu_buffer_rsrc_t Rq = make_rsrc(
+      static_cast<const Tin*>(a.q) + row0 * K,
+      (uint32_t)((span * K + K) * sizeof(Tin)));
+  const __amdgpu_buffer_rsrc_t Rk = make_rsrc(
+      static_cast<const Tin*>(a.k) + row0 * K,
+      (uint32_t)((span * K + K) * sizeof(Tin)));
+  const __amdgpu_buffer_rsrc_t Rv = make_rsrc(
+      static_cast<const Tin*>(a.v) + row0 * V,
+      (uint32_t)((span * V + V) * sizeof(Tin)));
+  const __amdgpu_buffer_rsrc_t Rg =
+      make_rsrc(a.g + row0 * K, (uint32_t)((span * K + K) * 4));
+  const __amdgpu_buffer_rsrc_t Rb =
+      make_rsrc(a.beta + row0, (uint32_t)((span + 1) * 4));
 
-  // Prefetch registers, one item ahead: g in the scan layout (channel sc,
-  // rows sseg*RPT + i), q/k/v as 8-element pieces, beta of row tid.
-  float rg[RPT];
-  Raw8<Tin> rq[PPT], rk[PPT], rv[PPT];
-  float rbeta = 0.f;
-  auto load_gvb = [&](const Rs& R) {
-    if (kFullScan || tid < SCAN_T) {
+  float gx[RPT][8], bt[RPT];
+  Raw8<Tin> rq[RPT], rk[RPT], rv[RPT];
+  if (active) {
 #pragma unroll
-      for (int i = 0; i < RPT; ++i)
-        rg[i] = buffer_load_f32(
-            R.g, (uint32_t)((((int64_t)(sseg * RPT + i) * H) * K + sc) * 4));
-    }
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + NT * i;
-      if (kFullPieces || p < NPIECE) {
-        const int pr = p / (K / 8), c0 = 8 * (p % (K / 8));
-        rv[i].load_buf(R.v,
-                       (uint32_t)(((int64_t)pr * H * V + c0) * sizeof(Tin)));
-      }
-    }
-    if (tid < C) rbeta = buffer_load_f32(R.b, (uint32_t)((int64_t)tid * H * 4));
-  };
-  auto load_qk = [&](const Rs& R) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + NT * i;
-      if (kFullPieces || p < NPIECE) {
-        const int pr = p / (K / 8), c0 = 8 * (p % (K / 8));
-        const uint32_t off =
-            (uint32_t)(((int64_t)pr * H * K + c0) * sizeof(Tin));
-        rq[i].load_buf(R.q, off);
-        rk[i].load_buf(R.k, off);
-      }
-    }
-  };
-  auto load_inputs = [&](const Rs& R) {
-    load_gvb(R);
-    load_qk(R);
-  };
-
-  // One item, with its inputs already in the prefetch registers; issues the
-  // prefetch of `nrs` as soon as the registers are free.
-  auto process = [&](const Item& it, const Rs& nrs) {
-    const int h = it.h;
-    const int64_t slot = it.t0 / C + it.n;
-    char* blk = a.ws + ((size_t)h * a.nslots + slot) * lay.block_bytes;
-    bf16* gW = reinterpret_cast<bf16*>(blk + lay.off_W);
-    bf16* gQh = reinterpret_cast<bf16*>(blk + lay.off_Qh);
-    bf16* gKbT = reinterpret_cast<bf16*>(blk + lay.off_KbT);
-    bf16* gUtT = reinterpret_cast<bf16*>(blk + lay.off_UtT);
-    bf16* gM = reinterpret_cast<bf16*>(blk + lay.off_M);
-    float* gGamma = reinterpret_cast<float*>(blk + lay.off_gamma);
-
-    __syncthreads();  // the previous item is done with every LDS buffer
-
-    // ---- 1. stage: decay scan, beta, q and k rows, (beta v)^T ------------
-    float loc[RPT];
-    if (kFullScan || tid < SCAN_T) {
-      float run = 0.f;
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        run += rg[i] * kLog2e;
-        loc[i] = run;
-      }
-      s_tot[sseg][sc] = run;
-    }
-    if (tid < C) s_beta[tid] = rbeta;
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + NT * i;
-      if (kFullPieces || p < NPIECE) {
-        const int pr = p / (K / 8), c0 = 8 * (p % (K / 8));
-        float x[8];
-        rk[i].get(x);
-        lds_put8(&s_k[pr][c0], x);
-      }
-    }
-    __syncthreads();
-    if (kFullScan || tid < SCAN_T) {
-      float off = 0.f;
-#pragma unroll
-      for (int j = 0; j < TPC - 1; ++j)
-        if (j < sseg) off += s_tot[j][sc];
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) s_a[sseg * RPT + i][sc] = loc[i] + off;
-    }
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + NT * i;
-      if (kFullPieces || p < NPIECE) {
-        const int pr = p / (V / 8), c0 = 8 * (p % (V / 8));
-        float x[8];
-        rv[i].get(x);
-        const float b = s_beta[pr];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          s_vbT[c0 + e][vswz(c0 + e, pr)] = (bf16)(b * x[e]);
-      }
-    }
-    load_gvb(nrs);  // g, v, beta registers are free now
-    __syncthreads();
-
-    // ---- 2. gamma, Q^ and K-bar^T (workspace), (beta k e^a)^T (LDS) ------
-    // gamma: every thread stores; threads past d_k fall outside the buffer.
-    __builtin_amdgcn_raw_buffer_store_b32(
-        __builtin_bit_cast(unsigned, __builtin_amdgcn_exp2f(s_a[C - 1][tid % K])),
-        make_rsrc(gGamma, K * 4), (uint32_t)(tid * 4), 0, 0);
-    // Q^ = q e^a (workspace) and the row operands k e^{a - rho}, q e^{a - rho}
-    // (LDS), rho = the decay just before the row's 16-row sub-tile.
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + NT * i;
-      if (kFullPieces || p < NPIECE) {
-        const int pr = p / (K / 8), c0 = 8 * (p % (K / 8));
-        const int rb = pr & ~15;  // first row of the sub-tile
-        float x[8], kx[8], av[8], rho[8];
-        rq[i].get(x);
-        rk[i].get(kx);
-        lds_get8(&s_a[pr][c0], av);
-        if (rb > 0) {
-          lds_get8(&s_a[rb - 1][c0], rho);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) rho[e] = 0.f;
-        }
-        float qh[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float f = __builtin_amdgcn_exp2f(av[e] - rho[e]);
-          qh[e] = x[e] * __builtin_amdgcn_exp2f(av[e]);
-          x[e] *= f;
-          kx[e] *= f;
-        }
-        *reinterpret_cast<bf16x8*>(gQh + WsLayout::frag16(pr, c0, lay.kst)) =
-            pack8(qh);
-        *reinterpret_cast<bf16x8*>(&s_qh[pr][c0]) = pack8(x);
-        *reinterpret_cast<bf16x8*>(&s_kh[pr][c0]) = pack8(kx);
-      }
-    }
-    load_qk(nrs);  // q, k registers are free now
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + NT * i;
-      if (kFullPieces || p < NPIECE) {
-        const int c = p % K, s0 = 8 * (p / K);
-        const float alast = s_a[C - 1][c];
-        float kb[8], kh[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int s = s0 + e;
-          const float kv = (float)s_k[s][c];
-          const float as = s_a[s][c];
-          kb[e] = kv * __builtin_amdgcn_exp2f(alast - as);
-          kh[e] = s_beta[s] * kv * __builtin_amdgcn_exp2f(as);
-        }
-        *reinterpret_cast<bf16x8*>(gKbT + WsLayout::frag16(c, s0, lay.cst)) =
-            pack8(kb);
-        *reinterpret_cast<bf16x8*>(&s_kbT[c][s0]) = pack8(kh);
-      }
-    }
-    __syncthreads();  // row operands complete
-
-    // ---- 3. A (LDS, fp32) and M (workspace, bf16).  Jobs: the NPAIR tile
-    //         pairs (m, n <= m), then the NUP tiles of M above the diagonal
-    //         (zero); job j runs on wave j % NW, every job stores one tile of
-    //         M, and every wave runs the same number of jobs. ---------------
-#pragma unroll
-    for (int jj = 0; jj < NJOBW; ++jj) {
-      const int job = wave + NW * jj;
-      if (job < NPAIR) {
-        int m = 0;
-        while ((m + 1) * (m + 2) / 2 <= job) ++m;
-        const int nn = job - m * (m + 1) / 2;
-        const int r = 16 * m + rl, s = 16 * nn + rl;
-        f32x4 accA = zero4(), accMT = zero4();
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          const int c0 = 32 * ks + 8 * kg;
-          bf16x8 kr = zero_bf16x8(), qr = zero_bf16x8();
-          float kc[8];
-          if (kFullK || c0 < K) {
-            float as[8], rho[8];
-            kr = *reinterpret_cast<const bf16x8*>(&s_kh[r][c0]);
-            qr = *reinterpret_cast<const bf16x8*>(&s_qh[r][c0]);
-            lds_get8(&s_k[s][c0], kc);
-            lds_get8(&s_a[s][c0], as);
-            if (m > 0) {
-              lds_get8(&s_a[16 * m - 1][c0], rho);
-            } else {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) rho[e] = 0.f;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              kc[e] *= __builtin_amdgcn_exp2f(rho[e] - as[e]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) kc[e] = 0.f;
-          }
-          const bf16x8 kcb = pack8(kc);
-          accA = mfma_bf16(kr, kcb, accA);    // A tile: rows r, cols s
-          accMT = mfma_bf16(kcb, qr, accMT);  // M^T tile: rows s, cols r
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rr = 16 * m + 4 * kg + e, ss = 16 * nn + rl;
-          s_A[rr][ss] = ss < rr ? s_beta[rr] * accA[e] : 0.f;
-        }
-        bf16x4 mv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ss = 16 * nn + 4 * kg + e;
-          mv[e] = (bf16)(ss <= r ? accMT[e] : 0.f);
-        }
-        *reinterpret_cast<bf16x4*>(
-            gM + WsLayout::frag16(r, 16 * nn + 4 * kg, lay.cst)) = mv;
-      } else if (job < NPAIR + NUP) {
-        int z = job - NPAIR, m = 0;  // z-th tile above the diagonal
-        while (z >= NSUB - 1 - m) {
-          z -= NSUB - 1 - m;
-          ++m;
-        }
-        const int nn = m + 1 + z;
-        *reinterpret_cast<uint2*>(
-            gM + WsLayout::frag16(16 * m + rl, 16 * nn + 4 * kg, lay.cst)) =
-            make_uint2(0u, 0u);
-      }
-    }
-    __syncthreads();  // A complete; the decay buffer is no longer read
-
-    // ---- 4. INV = (I + A)^-1 in fp32 (s_inv) and bf16 (s_invb): diagonal
-    //         16x16 blocks by forward substitution (one column per lane),
-    //         then off-diagonal blocks by levels:
-    //         INV_mn = -INV_mm * sum_{j=n}^{m-1} A_mj INV_jn ----------------
-    if (wave < NSUB && lane < 16) {
-      const int m = wave, j = lane, b = 16 * m;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = (r == j) ? 1.f : 0.f;
-#pragma unroll
-        for (int s2 = 0; s2 < r; ++s2) acc -= s_A[b + r][b + s2] * x[s2];
-        x[r] = acc;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s_inv[b + r][b + j] = x[r];
-        s_invb[b + r][b + j] = (bf16)x[r];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int d = 1; d < NSUB; ++d) {
-      const int nb = wave, mb = wave + d;
-      if (mb < NSUB) {
-        f32x4 t = zero4();
-        for (int j = nb; j < mb; ++j) {
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            t = mfma_f32(s_A[16 * mb + rl][16 * j + 4 * kk + kg],
-                         s_inv[16 * j + 4 * kk + kg][16 * nb + rl], t);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s_tmp[wave][4 * kg + e][rl] = t[e];
-        f32x4 u = zero4();
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          u = mfma_f32(s_inv[16 * mb + rl][16 * mb + 4 * kk + kg],
-                       s_tmp[wave][4 * kk + kg][rl], u);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s_inv[16 * mb + 4 * kg + e][16 * nb + rl] = -u[e];
-          s_invb[16 * mb + 4 * kg + e][16 * nb + rl] = (bf16)(-u[e]);
-        }
-      }
-      __syncthreads();
-    }
-
-    // ---- 5. W = INV (beta k e^a) (row-major, via W^T tiles) and
-    //         U~ = INV (beta v) (stored transposed) ------------------------
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int t = wave + NW * i;  // interleaved: every wave sees every m
-      if (NTILE % NW == 0 || t < NTILE) {
-        const int m = t / (KT + VT), ct = t % (KT + VT);
-        const bool isW = ct < KT;
-        const int col = 16 * (isW ? ct : ct - KT) + rl;
-        const int r = 16 * m + rl;
-        const int csteps = (16 * (m + 1) + 31) / 32;
-        f32x4 acc = zero4();
-        for (int cs = 0; cs < csteps; ++cs) {
-          const int s0 = 32 * cs + 8 * kg;
-          bf16x8 iv = zero_bf16x8(), bv = zero_bf16x8();
-          if (s0 < C) {
-            iv = *reinterpret_cast<const bf16x8*>(&s_invb[r][s0]);
-            bv = *reinterpret_cast<const bf16x8*>(
-                isW ? &s_kbT[col][s0] : &s_vbT[col][vswz(col, s0)]);
-          }
-          acc = isW ? mfma_bf16(bv, iv, acc)   // W^T tile: rows c, cols r
-                    : mfma_bf16(iv, bv, acc);  // U~ tile: rows r, cols j
-        }
-        bf16x4 ov;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (bf16)acc[e];
-        if (isW) {
-          *reinterpret_cast<bf16x4*>(
-              gW + WsLayout::frag16(r, 16 * ct + 4 * kg, lay.kst)) = ov;
-        } else {
-          *reinterpret_cast<bf16x4*>(
-              gUtT + WsLayout::frag_ut(col, 16 * m + 4 * kg, lay.mt)) = ov;
-        }
-      }
-    }
-  };
-
-  int64_t item = blockIdx.x;
-  if (!kVarlen) {
-    // Every item is valid.  The first item is peeled so that both paths into
-    // the loop header have the same shape (prefetch loads, then one item's
-    // stores): the compiler then waits only for the loads it needs and never
-    // drains the previous item's stores.
-    if (item >= total_items) return;
-    Item it = decode_item<kVarlen>(a, C, item);
-    load_inputs(item_rsrc(it));
-    int64_t next = item + gridDim.x;
-    bool more = next < total_items;
-    Item nx = decode_item<kVarlen>(a, C, more ? next : item);
-    process(it, item_rsrc(nx));  // peeled; the last item reloads its inputs
-    while (more) {
-      item = next;
-      it = nx;
-      next = item + gridDim.x;
-      more = next < total_items;
-      nx = decode_item<kVarlen>(a, C, more ? next : item);
-      process(it, item_rsrc(nx));
+    for (int i = 0; i < RPT; ++i) {
+      const uint32_t row = (uint32_t)((r0 + i) * H);
+      const uint4 g0 = buffer_load_16(Rg, (row * K + c0) * 4);
+      const uint4 g1 = buffer_load_16(Rg, (row * K + c0 + 4) * 4);
+      gx[i][0] = __uint_as_float(g0.x); gx[i][1] = __uint_as_float(g0.y);
+      gx[i][2] = __uint_as_float(g0.z); gx[i][3] = __uint_as_float(g0.w);
+      gx[i][4] = __uint_as_float(g1.x); gx[i][5] = __uint_as_float(g1.y);
+      gx[i][6] = __uint_as_float(g1.z); gx[i][7] = __uint_as_float(g1.w);
+      rq[i].load_buf(Rq, (row * K + c0) * sizeof(Tin));
+      rk[i].load_buf(Rk, (row * K + c0) * sizeof(Tin));
+      rv[i].load_buf(Rv, (row * V + c0) * sizeof(Tin));
+      bt[i] = buffer_load_f32(Rb, row * 4);
     }
   } else {
-    bool have = false;  // prefetch registers hold `item`'s inputs
-    if (item < total_items) {
-      const Item it = decode_item<kVarlen>(a, C, item);
-      if (it.valid) {
-        load_inputs(item_rsrc(it));
-        have = true;
-      }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gx[i][e] = 0.f;
+      rq[i].zero();
+      rk[i].zero();
+      rv[i].zero();
+      bt[i] = 0.f;
     }
-    for (; item < total_items; item += gridDim.x) {
-      const Item it = decode_item<kVarlen>(a, C, item);
-      if (!it.valid) continue;  // uniform across the workgroup
-      if (!have) load_inputs(item_rsrc(it));
-      const int64_t next = item + gridDim.x;
-      const int64_t nclamp = next < total_items ? next : item;
-      const Item nx = decode_item<kVarlen>(a, C, nclamp);
-      have = next < total_items && nx.valid;
-      process(it, item_rsrc(nx.valid ? nx : it));
+  }
+
+  // ---- 1. cumulative log2-decay a (registers): inclusive scan over the
+  //         thread's rows, then over the lanes of the wave that hold the
+  //         same channels (row groups in order), then over the waves --------
+  float run[8], inc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) run[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      run[e] += gx[i][e] * kLog2e;
+      gx[i][e] = run[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) inc[e] = run[e];
+#pragma unroll
+  for (int d = CGN; d < kWave; d <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float y = __shfl_up(inc[e], d);
+      if (lane >= d) inc[e] += y;
+    }
+  }
+  if (lane >= kWave - CGN) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_wtot[wave][c0 + e] = inc[e];
+  }
+  __syncthreads();
+  float off[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) off[e] = inc[e] - run[e];
+#pragma unroll
+  for (int w = 0; w < NW - 1; ++w) {
+    if (w < wave) {
+      float t[8];
+      lds_get8(&s_wtot[w][c0], t);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) off[e] += t[e];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gx[i][e] += off[e];  // gx now holds a
+  }
+  // decay references: rho_j = a_{16j-1} from the thread owning that row
+  if (active) {
+    if (r0 == 0) {
+      float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      lds_put8(&s_rho[0][c0], z);
+    }
+    if ((r0 + RPT) % 16 == 0) lds_put8(&s_rho[(r0 + RPT) / 16][c0], gx[RPT - 1]);
+    if (cg == 0) {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) s_beta[r0 + i] = bt[i];
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. exponentiated operands from registers: Q^ and K-bar^T and gamma
+  //         (workspace), row operands and column base (LDS), beta k e^a and
+  //         beta v kept for stage 4 ------------------------------------------
+  float kbT[8][RPT], vbT[8][RPT];
+  if (active) {
+    const int m = r0 >> 4;  // the thread's rows lie in one sub-tile
+    float rho[8], rho1[8], alast[8];
+    lds_get8(&s_rho[m][c0], rho);
+    lds_get8(&s_rho[m + 1][c0], rho1);
+    lds_get8(&s_rho[NSUB][c0], alast);
+    float kbar[8][RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = r0 + i;
+      float q[8], k[8], v[8], qh[8], kh[8], kc[8], qe[8];
+      rq[i].get(q);
+      rk[i].get(k);
+      rv[i].get(v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float av = gx[i][e];
+        const float f = __builtin_amdgcn_exp2f(av - rho[e]);
+        const float ea = __builtin_amdgcn_exp2f(av);
+        qh[e] = q[e] * f;
+        kh[e] = k[e] * f;
+        kc[e] = k[e] * __builtin_amdgcn_exp2f(rho1[e] - av);
+        qe[e] = q[e] * ea;
+        kbar[e][i] = k[e] * __builtin_amdgcn_exp2f(alast[e] - av);
+        kbT[e][i] = bt[i] * k[e] * ea;
+        vbT[e][i] = bt[i] * v[e];
+      }
+      *reinterpret_cast<bf16x8*>(&s_qh[r][c0]) = pack8(qh);
+      *reinterpret_cast<bf16x8*>(&s_kh[r][c0]) = pack8(kh);
+      *reinterpret_cast<bf16x8*>(&s_kcb[r][c0]) = pack8(kc);
+      *reinterpret_cast<bf16x8*>(gQh + WsLayout::frag16(r, c0, lay.kst)) =
+          pack8(qe);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      store_bf16xn<RPT>(gKbT + WsLayout::frag16(c0 + e, r0, lay.cst), kbar[e]);
+    if (r0 == 0) {
+      float gam[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gam[e] = __builtin_amdgcn_exp2f(alast[e]);
+      *reinterpret_cast<float4*>(gGamma + c0) =
+          make_float4(gam[0], gam[1], gam[2], gam[3]);
+      *reinterpret_cast<float4*>(gGamma + c0 + 4) =
+          make_float4(gam[4], gam[5], gam[6], gam[7]);
+    }
+  }
+  __syncthreads();  // operands complete
+
+  // ---- 3. A (LDS, fp32) and M (workspace, bf16).  Jobs: the NPAIR tile
+  //         pairs (m, n <= m), then the NUP tiles of M above the diagonal
+  //         (zero); job j runs on wave j % NW. -------------------------------
+#pragma unroll
+  for (int jj = 0; jj < NJOBW; ++jj) {
+    const int job = wave + NW * jj;
+    if (job < NPAIR) {
+      int m = 0;
+      while ((m + 1) * (m + 2) / 2 <= job) ++m;
+      const int nn = job - m * (m + 1) / 2;
+      const int r = 16 * m + rl, s = 16 * nn + rl;
+      f32x4 accA = zero4(), accMT = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int cc = 32 * ks + 8 * kg;
+        bf16x8 kr = zero_bf16x8(), qr = zero_bf16x8();
+        float kc[8];
+        if (kFullK || cc < K) {
+          float fm[8], fn[8];
+          kr = *reinterpret_cast<const bf16x8*>(&s_kh[r][cc]);
+          qr = *reinterpret_cast<const bf16x8*>(&s_qh[r][cc]);
+          lds_get8(&s_kcb[s][cc], kc);
+          lds_get8(&s_rho[m][cc], fm);
+          lds_get8(&s_rho[nn + 1][cc], fn);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            kc[e] *= __builtin_amdgcn_exp2f(fm[e] - fn[e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kc[e] = 0.f;
+        }
+        const bf16x8 kcb = pack8(kc);
+        accA = mfma_bf16(kr, kcb, accA);    // A tile: rows r, cols s
+        accMT = mfma_bf16(kcb, qr, accMT);  // M^T tile: rows s, cols r
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = 16 * m + 4 * kg + e, ss = 16 * nn + rl;
+        s_A[rr][ss] = ss < rr ? s_beta[rr] * accA[e] : 0.f;
+      }
+      bf16x4 mv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ss = 16 * nn + 4 * kg + e;
+        mv[e] = (bf16)(ss <= r ? accMT[e] : 0.f);
+      }
+      *reinterpret_cast<bf16x4*>(
+          gM + WsLayout::frag16(r, 16 * nn + 4 * kg, lay.cst)) = mv;
+    } else if (job < NPAIR + NUP) {
+      int z = job - NPAIR, m = 0;  // z-th tile above the diagonal
+      while (z >= NSUB - 1 - m) {
+        z -= NSUB - 1 - m;
+        ++m;
+      }
+      const int nn = m + 1 + z;
+      *reinterpret_cast<uint2*>(
+          gM + WsLayout::frag16(16 * m + rl, 16 * nn + 4 * kg, lay.cst)) =
+          make_uint2(0u, 0u);
+    }
+  }
+  __syncthreads();  // A complete; the row operands and column base are dead
+
+  // ---- 4. (beta k e^a)^T and (beta v)^T into LDS; INV = (I + A)^-1 in
+  //         fp32: diagonal 16x16 blocks by forward substitution (one column
+  //         per lane), then off-diagonal blocks by levels:
+  //         INV_mn = -INV_mm * sum_{j=n}^{m-1} A_mj INV_jn -------------------
+  if (active) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = c0 + e;
+      store_bf16xn<RPT>(&s_kbT[c][swz(c, r0)], kbT[e]);
+      store_bf16xn<RPT>(&s_vbT[c][swz(c, r0)], vbT[e]);
+    }
+  }
+  if (wave < NSUB && lane < 16) {
+    const int m = wave, j = lane, b = 16 * m;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < r; ++s2) acc -= s_A[b + r][b + s2] * x[s2];
+      x[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s_inv[b + r][b + j] = x[r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int d = 1; d < NSUB; ++d) {
+    const int nb = wave, mb = wave + d;
+    if (mb < NSUB) {
+      f32x4 t = zero4();
+      for (int j = nb; j < mb; ++j) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          t = mfma_f32(s_A[16 * mb + rl][16 * j + 4 * kk + kg],
+                       s_inv[16 * j + 4 * kk + kg][16 * nb + rl], t);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_tmp[wave][4 * kg + e][rl] = t[e];
+      f32x4 u = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        u = mfma_f32(s_inv[16 * mb + rl][16 * mb + 4 * kk + kg],
+                     s_tmp[wave][4 * kk + kg][rl], u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        s_inv[16 * mb + 4 * kg + e][16 * nb + rl] = -u[e];
+    }
+    __syncthreads();
+  }
+  // INV to bf16 in A's storage (A is dead), zero above the diagonal blocks
+  for (int e = tid; e < C * C; e += NT) {
+    const int r = e / C, c = e % C;
+    s_invb[r][c] = (c >> 4) > (r >> 4) ? (bf16)0.f : (bf16)s_inv[r][c];
+  }
+  __syncthreads();
+
+  // ---- 5. W = INV (beta k e^a) (row-major, via W^T tiles) and
+  //         U~ = INV (beta v) (stored transposed) ----------------------------
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int t = wave + NW * i;  // interleaved: every wave sees every m
+    if (NTILE % NW == 0 || t < NTILE) {
+      const int m = t / (KT + VT), ct = t % (KT + VT);
+      const bool isW = ct < KT;
+      const int col = 16 * (isW ? ct : ct - KT) + rl;
+      const int r = 16 * m + rl;
+      const int csteps = (16 * (m + 1) + 31) / 32;
+      f32x4 acc = zero4();
+      for (int cs = 0; cs < csteps; ++cs) {
+        const int s0 = 32 * cs + 8 * kg;
+        bf16x8 iv = zero_bf16x8(), bv = zero_bf16x8();
+        if (s0 < C) {
+          iv = *reinterpret_cast<const bf16x8*>(&s_invb[r][s0]);
+          bv = *reinterpret_cast<const bf16x8*>(
+              isW ? &s_kbT[col][swz(col, s0)] : &s_vbT[col][swz(col, s0)]);
+        }
+        acc = isW ? mfma_bf16(bv, iv, acc)   // W^T tile: rows c, cols r
+                  : mfma_bf16(iv, bv, acc);  // U~ tile: rows r, cols j
+      }
+      bf16x4 ov;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[e] = (bf16)acc[e];
+      if (isW) {
+        *reinterpret_cast<bf16x4*>(
+            gW + WsLayout::frag16(r, 16 * ct + 4 * kg, lay.kst)) = ov;
+      } else {
+        *reinterpret_cast<bf16x4*>(
+            gUtT + WsLayout::frag_ut(col, 16 * m + 4 * kg, lay.mt)) = ov;
+      }
     }
   }
 }
 
-// Persistent launch: as many workgroups as fit on the device at once, each
-// walking the work items with a stride of the grid size.
-template <typename Tin, int D, int C, bool kVarlen>
-hipError_t launch_v(const PrefillArgs& a, hipStream_t st) {
-  const int64_t items = (int64_t)a.N * a.max_chunks * a.H;
-  int dev = 0, cus = 0, per_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess)
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void*>(prep_kernel<Tin, D, C, kVarlen>),
-        512, 0);
-  if (e != hipSuccess) return e;
-  const int64_t resident = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
-  const unsigned grid = (unsigned)(items < resident ? items : resident);
-  void* args[] = {const_cast<PrefillArgs*>(&a), const_cast<int64_t*>(&items)};
-  return hipLaunchKernel(
-      reinterpret_cast<const void*>(prep_kernel<Tin, D, C, kVarlen>),
-      dim3(grid), dim3(512), args, 0, st);
-}
-
+// One workgroup per (sequence, chunk, head) item; items past the end of a
+// packed sequence exit at once.
 template <typename Tin, int D, int C>
 hipError_t launch(const PrefillArgs& a, hipStream_t st) {
-  return a.cu_seqlens ? launch_v<Tin, D, C, true>(a, st)
-                      : launch_v<Tin, D, C, false>(a, st);
+  const int64_t items = (int64_t)a.N * a.max_chunks * a.H;
+  return launch_kernel(prep_kernel<Tin, D, C>, dim3((unsigned)items),
+                       dim3(256), st, a);
 }
 
 template <typename Tin, int D>
