@@ -119,14 +119,17 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
 
   // LDS.  Region R is reused across phases:
   //   scan:        wave totals [NW][D] fp32
-  //   stages 1-3:  qh, kh, kcb [C][RP] bf16 (row operands, column base)
+  //   stages 1-3:  qh, kh, kcb [C][RP] bf16 (row operands, column base),
+  //                pair factors [NPAIR][D] fp32
   //   stages 4-5:  kbT, vbT [D][TP] bf16, INV [C][AP] fp32, tmp [NSUB][16][20]
   constexpr int R_OPS = 3 * C * RP * 2;
+  constexpr int R_F = R_OPS, R_EARLY = R_F + NPAIR * D * 4;
   constexpr int R_KB = 0, R_VB = D * TP * 2, R_INV = 2 * D * TP * 2;
   constexpr int R_TMP = R_INV + C * AP * 4;
   constexpr int R_LATE = R_TMP + NSUB * 16 * 20 * 4;
-  constexpr int R_BYTES = R_OPS > R_LATE ? (R_OPS > NW * D * 4 ? R_OPS : NW * D * 4)
-                                         : (R_LATE > NW * D * 4 ? R_LATE : NW * D * 4);
+  constexpr int R_BYTES =
+      R_EARLY > R_LATE ? (R_EARLY > NW * D * 4 ? R_EARLY : NW * D * 4)
+                       : (R_LATE > NW * D * 4 ? R_LATE : NW * D * 4);
   __shared__ __attribute__((aligned(16))) char s_r[R_BYTES];
   __shared__ __attribute__((aligned(16))) float s_A[C][AP];  // later INV bf16
   __shared__ __attribute__((aligned(16))) float s_rho[NSUB + 1][D];
@@ -135,6 +138,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
   bf16 (*s_qh)[RP] = reinterpret_cast<bf16 (*)[RP]>(s_r);
   bf16 (*s_kh)[RP] = reinterpret_cast<bf16 (*)[RP]>(s_r + C * RP * 2);
   bf16 (*s_kcb)[RP] = reinterpret_cast<bf16 (*)[RP]>(s_r + 2 * C * RP * 2);
+  float (*s_f)[D] = reinterpret_cast<float (*)[D]>(s_r + R_F);
   bf16 (*s_kbT)[TP] = reinterpret_cast<bf16 (*)[TP]>(s_r + R_KB);
   bf16 (*s_vbT)[TP] = reinterpret_cast<bf16 (*)[TP]>(s_r + R_VB);
   float (*s_inv)[AP] = reinterpret_cast<float (*)[AP]>(s_r + R_INV);
@@ -274,6 +278,15 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
   // ---- 2. exponentiated operands from registers: Q^ and K-bar^T and gamma
   //         (workspace), row operands and column base (LDS), beta k e^a and
   //         beta v kept for stage 4 ------------------------------------------
+  // factor of tile pair p = (m, n <= m), p = m (m + 1) / 2 + n:
+  // e^{rho_m - rho_{n+1}} per channel
+  for (int e = tid; e < NPAIR * D; e += NT) {
+    const int p = e / D, c = e % D;
+    int m = 0;
+    while ((m + 1) * (m + 2) / 2 <= p) ++m;
+    const int nn = p - m * (m + 1) / 2;
+    s_f[p][c] = __builtin_amdgcn_exp2f(s_rho[m][c] - s_rho[nn + 1][c]);
+  }
   float kbT[8][RPT], vbT[8][RPT];
   if (active) {
     const int m = r0 >> 4;  // the thread's rows lie in one sub-tile
@@ -341,15 +354,13 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
         bf16x8 kr = zero_bf16x8(), qr = zero_bf16x8();
         float kc[8];
         if (kFullK || cc < K) {
-          float fm[8], fn[8];
+          float f[8];
           kr = *reinterpret_cast<const bf16x8*>(&s_kh[r][cc]);
           qr = *reinterpret_cast<const bf16x8*>(&s_qh[r][cc]);
           lds_get8(&s_kcb[s][cc], kc);
-          lds_get8(&s_rho[m][cc], fm);
-          lds_get8(&s_rho[nn + 1][cc], fn);
+          lds_get8(&s_f[job][cc], f);
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            kc[e] *= __builtin_amdgcn_exp2f(fm[e] - fn[e]);
+          for (int e = 0; e < 8; ++e) kc[e] *= f[e];
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) kc[e] = 0.f;
@@ -435,10 +446,20 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
     }
     __syncthreads();
   }
-  // INV to bf16 in A's storage (A is dead), zero above the diagonal blocks
-  for (int e = tid; e < C * C; e += NT) {
-    const int r = e / C, c = e % C;
-    s_invb[r][c] = (c >> 4) > (r >> 4) ? (bf16)0.f : (bf16)s_inv[r][c];
+  // INV to bf16 in A's storage (A is dead), zero above the diagonal blocks;
+  // one 16-column segment of a row per thread
+  for (int e = tid; e < C * C / 16; e += NT) {
+    const int r = e / (C / 16), c = 16 * (e % (C / 16));
+    float x[16];
+    if ((c >> 4) > (r >> 4)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = 0.f;
+    } else {
+      lds_get8(&s_inv[r][c], *reinterpret_cast<float(*)[8]>(&x[0]));
+      lds_get8(&s_inv[r][c + 8], *reinterpret_cast<float(*)[8]>(&x[8]));
+    }
+    lds_put8(&s_invb[r][c], *reinterpret_cast<float(*)[8]>(&x[0]));
+    lds_put8(&s_invb[r][c + 8], *reinterpret_cast<float(*)[8]>(&x[8]));
   }
   __syncthreads();
 

@@ -186,7 +186,21 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
         (uint32_t)(((int64_t)(L - 1) * H * V + BV) * sizeof(Tout)));
     __syncthreads();  // S^T copy complete; U^T buffer free
 
-    // U = U~ - W S,  O^T = S^T Q^^T
+    // U = U~ - W S,  O^T = S^T Q^^T.  Every S^T fragment of the phase is
+    // read before the first product so that the LDS latencies overlap.
+    bf16x8 sbf[UPW][KSTEPS];
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      const int jt = (u0 + i) % JT;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        // per-lane guards only select operands; every lane runs the MFMA
+        const int c0 = 32 * kk + 8 * kg;
+        sbf[i][kk] = zero_bf16x8();
+        if ((kAllU || u0 + i < NUT) && (kFullK || c0 < K))
+          sbf[i][kk] = *reinterpret_cast<const bf16x8*>(&s_SbT[16 * jt + rl][c0]);
+      }
+    }
     f32x4 Ot[UPW];
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
@@ -196,13 +210,8 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
         f32x4 wsacc = zero4();
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-          // per-lane guards only select operands; every lane runs the MFMA
-          const int c0 = 32 * kk + 8 * kg;
-          bf16x8 sb = zero_bf16x8();
-          if (kFullK || c0 < K)
-            sb = *reinterpret_cast<const bf16x8*>(&s_SbT[16 * jt + rl][c0]);
-          wsacc = mfma_bf16(op.w[kk], sb, wsacc);
-          Ot[i] = mfma_bf16(sb, op.qh[kk], Ot[i]);
+          wsacc = mfma_bf16(op.w[kk], sbf[i][kk], wsacc);
+          Ot[i] = mfma_bf16(sbf[i][kk], op.qh[kk], Ot[i]);
         }
         const bf16x4 ut = __builtin_bit_cast(bf16x4, op.ut[i]);
         bf16x4 ub;
@@ -214,19 +223,27 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
     }
     __syncthreads();  // U^T complete
 
+    // U^T fragments, read once for both products below
+    bf16x8 ubf[JT][CSTEPS];
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+#pragma unroll
+      for (int cs = 0; cs < CSTEPS; ++cs) {
+        const int s0 = 32 * cs + 8 * kg;
+        ubf[jt][cs] = zero_bf16x8();
+        if (kFullC || s0 < C)
+          ubf[jt][cs] = *reinterpret_cast<const bf16x8*>(&s_UbT[16 * jt + rl][s0]);
+      }
+    }
+
     // O^T += U^T M^T; store O (rows >= L fall outside the buffer: dropped)
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
       if (kAllU || u0 + i < NUT) {
         const int jt = (u0 + i) % JT;
 #pragma unroll
-        for (int cs = 0; cs < CSTEPS; ++cs) {
-          const int s0 = 32 * cs + 8 * kg;
-          bf16x8 ubv = zero_bf16x8();
-          if (kFullC || s0 < C)
-            ubv = *reinterpret_cast<const bf16x8*>(&s_UbT[16 * jt + rl][s0]);
-          Ot[i] = mfma_bf16(ubv, op.m[cs], Ot[i]);
-        }
+        for (int cs = 0; cs < CSTEPS; ++cs)
+          Ot[i] = mfma_bf16(ubf[jt][cs], op.m[cs], Ot[i]);
         const int r = 16 * mrow + rl;
         buffer_store4(o, orsrc,
                       (uint32_t)(((int64_t)r * H * V + 16 * jt + 4 * kg) *
@@ -249,13 +266,8 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
         const float4 gm = op.gm[lc];
         S[i][0] *= gm.x; S[i][1] *= gm.y; S[i][2] *= gm.z; S[i][3] *= gm.w;
 #pragma unroll
-        for (int cs = 0; cs < CSTEPS; ++cs) {
-          const int s0 = 32 * cs + 8 * kg;
-          bf16x8 ubv = zero_bf16x8();
-          if (kFullC || s0 < C)
-            ubv = *reinterpret_cast<const bf16x8*>(&s_UbT[16 * jt + rl][s0]);
-          S[i] = mfma_bf16(op.kb[lc][cs], ubv, S[i]);
-        }
+        for (int cs = 0; cs < CSTEPS; ++cs)
+          S[i] = mfma_bf16(op.kb[lc][cs], ubf[jt][cs], S[i]);
         bf16x4 sb;
 #pragma unroll
         for (int e = 0; e < 4; ++e) sb[e] = (bf16)S[i][e];
@@ -329,7 +341,7 @@ hipError_t launch_bv(const PrefillArgs& a, hipStream_t st) {
 // do more matrix work per chunk loaded; narrower ones give more workgroups
 // when there are few (sequence, head) pairs.  Measured on MI355X: 96 heads
 // run fastest at 64 (192 workgroups), 32 heads at 16 (256 workgroups).
-// KDA_RECUR_BV (16 / 32 / 64) overrides the choice.
+// KDA_RECUR_BV (16 / 32 / 64 / 128) overrides the choice.
 inline int pick_bv(int D, int64_t units) {
   static const int forced = [] {
     const char* e = getenv("KDA_RECUR_BV");
@@ -344,7 +356,9 @@ inline int pick_bv(int D, int64_t units) {
     bv = 64;
   else if (D >= 32 && units * (D / 32) >= cus)
     bv = 32;
-  if ((forced == 16 || forced == 32 || forced == 64) && forced <= D) bv = forced;
+  if ((forced == 16 || forced == 32 || forced == 64 || forced == 128) &&
+      forced <= D)
+    bv = forced;
   return D == 16 ? 16 : bv;
 }
 
@@ -379,6 +393,9 @@ hipError_t launch_w(const PrefillArgs& a, hipStream_t st) {
 template <typename Tout, int D, int C>
 hipError_t launch(const PrefillArgs& a, hipStream_t st) {
   const int bv = pick_bv(D, (int64_t)a.N * a.H);
+  if constexpr (D >= 128) {
+    if (bv == 128) return launch_w<Tout, D, C, 128>(a, st);
+  }
   if constexpr (D >= 64) {
     if (bv == 64) return launch_w<Tout, D, C, 64>(a, st);
   }
