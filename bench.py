@@ -94,6 +94,9 @@ def main(argv=None):
                     help="prefill workload timed in each step")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the oracle on the host cores")
+    ap.add_argument("--no-back-to-back", action="store_true",
+                    help="skip the back-to-back decode measurement (so that "
+                         "a kernel trace sees only the timed steps)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB per "
                          "step (reference kernel for HBM counter scaling)")
@@ -207,17 +210,19 @@ def main(argv=None):
     # decode steps back to back (outside the timed region): the state traffic
     # of one step then overlaps the write-back of the previous one, the
     # sustained case of a decode-only server loop
-    n_b2b = max(3 * args.steps, 30)
-    for i in range(6):
-        decode(i)
-    b0, b1 = ev(), ev()
-    b0.record(stream)
-    for i in range(n_b2b):
-        decode(i)
-    b1.record(stream)
-    torch.cuda.synchronize()
-    b2b_ms = b0.elapsed_time(b1) / n_b2b
-    log("decode back to back: %.4f ms" % b2b_ms)
+    n_b2b, b2b_ms = 0, None
+    if not args.no_back_to_back:
+        n_b2b = max(3 * args.steps, 30)
+        for i in range(6):
+            decode(i)
+        b0, b1 = ev(), ev()
+        b0.record(stream)
+        for i in range(n_b2b):
+            decode(i)
+        b1.record(stream)
+        torch.cuda.synchronize()
+        b2b_ms = b0.elapsed_time(b1) / n_b2b
+        log("decode back to back: %.4f ms" % b2b_ms)
 
     # ---------------- derived figures --------------------------------------
     D, H = dp.K, dp.H
@@ -269,7 +274,7 @@ def main(argv=None):
             "traffic": traffic,
             "algorithmic_bytes_per_launch": dec_bytes,
             "avg_launch_ms": round(dec_avg, 5),
-            "back_to_back": {
+            "back_to_back": None if b2b_ms is None else {
                 "launches": n_b2b,
                 "avg_launch_ms": round(b2b_ms, 5),
                 "achieved": round(dec_bytes / (b2b_ms * 1e-3) / 1e9, 2),
