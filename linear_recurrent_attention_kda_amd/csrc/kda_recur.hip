@@ -122,42 +122,60 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
   const int64_t nchunks = (eos - bos + C - 1) / C;
   const char* ws_head = a.ws + (size_t)h * a.nslots * lay.block_bytes;
 
-  // Issue the loads of chunk ci's operands.  ci is clamped to the last
-  // chunk (a harmless duplicate load) instead of branching.
-  auto load_ops = [&](Ops& op, int64_t ci) {
+  // Loads of chunk ci's operands, in three groups issued as soon as the
+  // registers they fill are free: W, Q^ and U~ (read by the U phase), M (the
+  // O phase), K-bar^T and gamma (the state update).  Spreading them lets the
+  // address unit work through one group while the wave computes.  ci is
+  // clamped to the last chunk (a harmless duplicate load) instead of
+  // branching.
+  struct Blk {
+    const bf16 *W, *Qh, *KbT, *UtT, *M;
+    const float* G;
+  };
+  auto chunk_blk = [&](int64_t ci) {
     ci = ci < nchunks ? ci : nchunks - 1;
     const int64_t slot = (bos + ci * C) / C + n;
     const char* blk = ws_head + (size_t)slot * lay.block_bytes;
-    const bf16* gW = reinterpret_cast<const bf16*>(blk + lay.off_W);
-    const bf16* gQh = reinterpret_cast<const bf16*>(blk + lay.off_Qh);
-    const bf16* gKbT = reinterpret_cast<const bf16*>(blk + lay.off_KbT);
-    const bf16* gUtT = reinterpret_cast<const bf16*>(blk + lay.off_UtT);
-    const bf16* gM = reinterpret_cast<const bf16*>(blk + lay.off_M);
-    const float* gG = reinterpret_cast<const float*>(blk + lay.off_gamma);
+    Blk b;
+    b.W = reinterpret_cast<const bf16*>(blk + lay.off_W);
+    b.Qh = reinterpret_cast<const bf16*>(blk + lay.off_Qh);
+    b.KbT = reinterpret_cast<const bf16*>(blk + lay.off_KbT);
+    b.UtT = reinterpret_cast<const bf16*>(blk + lay.off_UtT);
+    b.M = reinterpret_cast<const bf16*>(blk + lay.off_M);
+    b.G = reinterpret_cast<const float*>(blk + lay.off_gamma);
+    return b;
+  };
+  auto load_u = [&](Ops& op, const Blk& b) {
     if (kAllU || has_u) {
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
         const int c0 = 32 * kk + 8 * kg;
         if (kFullK || c0 < K) {
           // fragment (mrow, kk), this lane's 16 bytes: one contiguous 1 KB
-          op.w[kk] = load_bf16x8(gW + ((mrow * lay.kst + kk) * 64 + lane) * 8);
-          op.qh[kk] = load_bf16x8(gQh + ((mrow * lay.kst + kk) * 64 + lane) * 8);
+          op.w[kk] = load_bf16x8(b.W + ((mrow * lay.kst + kk) * 64 + lane) * 8);
+          op.qh[kk] = load_bf16x8(b.Qh + ((mrow * lay.kst + kk) * 64 + lane) * 8);
         }
-      }
-#pragma unroll
-      for (int cs = 0; cs < CSTEPS; ++cs) {
-        const int s0 = 32 * cs + 8 * kg;   // M is zero above the diagonal
-        if (kFullC || s0 < C)
-          op.m[cs] = load_bf16x8(gM + ((mrow * lay.cst + cs) * 64 + lane) * 8);
       }
 #pragma unroll
       for (int i = 0; i < UPW; ++i) {
         const int jt = (u0 + i) % JT;
         if (kAllU || u0 + i < NUT)
           op.ut[i] = *reinterpret_cast<const uint2*>(
-              gUtT + ((((j0 >> 4) + jt) * lay.mt + mrow) * 64 + lane) * 4);
+              b.UtT + ((((j0 >> 4) + jt) * lay.mt + mrow) * 64 + lane) * 4);
       }
     }
+  };
+  auto load_m = [&](Ops& op, const Blk& b) {
+    if (kAllU || has_u) {
+#pragma unroll
+      for (int cs = 0; cs < CSTEPS; ++cs) {
+        const int s0 = 32 * cs + 8 * kg;   // M is zero above the diagonal
+        if (kFullC || s0 < C)
+          op.m[cs] = load_bf16x8(b.M + ((mrow * lay.cst + cs) * 64 + lane) * 8);
+      }
+    }
+  };
+  auto load_s = [&](Ops& op, const Blk& b) {
     if (kAllS || has_s) {
 #pragma unroll
       for (int lc = 0; lc < NCT; ++lc) {
@@ -167,17 +185,25 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
           const int s0 = 32 * cs + 8 * kg;
           if (kFullC || s0 < C)
             op.kb[lc][cs] =
-                load_bf16x8(gKbT + ((ct * lay.cst + cs) * 64 + lane) * 8);
+                load_bf16x8(b.KbT + ((ct * lay.cst + cs) * 64 + lane) * 8);
         }
-        op.gm[lc] = *reinterpret_cast<const float4*>(gG + 16 * ct + 4 * kg);
+        op.gm[lc] = *reinterpret_cast<const float4*>(b.G + 16 * ct + 4 * kg);
       }
     }
+  };
+  auto load_ops = [&](Ops& op, int64_t ci) {
+    const Blk b = chunk_blk(ci);
+    load_u(op, b);
+    load_m(op, b);
+    load_s(op, b);
   };
 
   Tout* o = static_cast<Tout*>(a.o);
 
-  // One chunk of the recurrence with its operands already in registers.
-  auto process = [&](const Ops& op, int64_t ci) {
+  // One chunk of the recurrence with its operands already in registers;
+  // each operand group is refilled with chunk `next` once consumed.
+  auto process = [&](Ops& op, int64_t ci, int64_t next) {
+    const Blk nb = chunk_blk(next);
     const int64_t t0 = bos + ci * C;
     const int L = (eos - t0) < C ? (int)(eos - t0) : C;
     // outputs of this chunk and slice: rows r < L at stride H*V elements
@@ -221,6 +247,7 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
             ub;
       }
     }
+    load_u(op, nb);
     __syncthreads();  // U^T complete
 
     // U^T fragments, read once for both products below
@@ -251,6 +278,7 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
                       Ot[i], a.scale);
       }
     }
+    load_m(op, nb);
 
     // S <- diag(gamma) S + K-bar^T U
 #pragma unroll
@@ -274,6 +302,7 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
         *reinterpret_cast<bf16x4*>(&s_SbT[16 * jt + rl][16 * ct + 4 * kg]) = sb;
       }
     }
+    load_s(op, nb);
   };
 
   // PF register sets: chunk ci computes while chunks ci + 1 .. ci + PF - 1
@@ -305,14 +334,11 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
     int64_t ci = 0;
     for (; ci + PF <= nchunks; ci += PF) {
 #pragma unroll
-      for (int f = 0; f < PF; ++f) {
-        process(ops[f], ci + f);
-        load_ops(ops[f], ci + f + PF);
-      }
+      for (int f = 0; f < PF; ++f) process(ops[f], ci + f, ci + f + PF);
     }
 #pragma unroll
     for (int f = 0; f < PF - 1; ++f)
-      if (ci + f < nchunks) process(ops[f], ci + f);
+      if (ci + f < nchunks) process(ops[f], ci + f, ci + f + PF);
   }
 
   if (a.final_state) {
