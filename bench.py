@@ -94,9 +94,14 @@ def main(argv=None):
                     help="prefill workload timed in each step")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the oracle on the host cores")
-    ap.add_argument("--no-back-to-back", action="store_true",
-                    help="skip the back-to-back decode measurement (so that "
-                         "a kernel trace sees only the timed steps)")
+    ap.add_argument("--ckpt-every", type=int, default=0,
+                    help="run the prefill through kda_prefill_varlen_ckpt, "
+                         "storing the state every N tokens (a multiple of "
+                         "the chunk size)")
+    ap.add_argument("--step-only", action="store_true",
+                    help="skip the measurements taken after the timed steps "
+                         "(back-to-back decode, reference copy), so that a "
+                         "kernel trace sees only the steps")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB per "
                          "step (reference kernel for HBM counter scaling)")
@@ -148,6 +153,16 @@ def main(argv=None):
         po = torch.empty((pp.B, pp.T, pp.H, pp.V), dtype=pq.dtype, device=dev)
     pfs = torch.empty((nseq, pp.H, pp.K, pp.V), dtype=torch.float32,
                       device=dev)
+    ck = None
+    if args.ckpt_every:
+        if pp.kind != "varlen":
+            cu = torch.arange(nseq + 1, dtype=torch.int32, device=dev) * pp.T
+            maxlen = pp.T
+        ck = torch.zeros((total // args.ckpt_every, pp.H, pp.K, pp.V),
+                         dtype=torch.float32, device=dev)
+        pq_, pk_, pv_ = (x.reshape(total, pp.H, -1) for x in (pq, pk, pv))
+        pg_, pbeta_ = pg.reshape(total, pp.H, -1), pbeta.reshape(total, pp.H)
+        po_ = po.reshape(total, pp.H, pp.V)
     ws = kda.workspace_for(nseq, total, pp.H, pp.K, pp.V, pp.C, dev)
     calib = None
     if args.calib_copy_mib:
@@ -159,7 +174,12 @@ def main(argv=None):
     stream = torch.cuda.current_stream(dev)
 
     def prefill():
-        if pp.kind == "varlen":
+        if ck is not None:
+            kda.kda_prefill_varlen_ckpt(pq_, pk_, pv_, pg_, pbeta_, cu, maxlen,
+                                        ps0, ckpt_every=args.ckpt_every,
+                                        chunk_size=pp.C, final_state=pfs,
+                                        o=po_, ckpt_states=ck, workspace=ws)
+        elif pp.kind == "varlen":
             kda.kda_prefill_varlen(pq, pk, pv, pg, pbeta, cu, maxlen, ps0,
                                    chunk_size=pp.C, final_state=pfs, o=po,
                                    workspace=ws)
@@ -204,14 +224,16 @@ def main(argv=None):
     ms_step = wall * 1e3 / args.steps
     pre_avg = float(np.mean(pre_ms))
     dec_avg = float(np.mean(dec_ms))
+    pre_med = float(np.median(pre_ms))
+    dec_med = float(np.median(dec_ms))
     log("timed %d steps: %.3f ms/step, prefill %.3f ms, decode %.4f ms"
         % (args.steps, ms_step, pre_avg, dec_avg))
 
     # decode steps back to back (outside the timed region): the state traffic
     # of one step then overlaps the write-back of the previous one, the
     # sustained case of a decode-only server loop
-    n_b2b, b2b_ms = 0, None
-    if not args.no_back_to_back:
+    n_b2b, b2b_ms, copy_ref = 0, None, None
+    if not args.step_only:
         n_b2b = max(3 * args.steps, 30)
         for i in range(6):
             decode(i)
@@ -223,6 +245,22 @@ def main(argv=None):
         torch.cuda.synchronize()
         b2b_ms = b0.elapsed_time(b1) / n_b2b
         log("decode back to back: %.4f ms" % b2b_ms)
+        # reference: the runtime's device-to-device copy of 1 GiB
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        c0, c1 = ev(), ev()
+        c0.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_ms = c0.elapsed_time(c1) / 10
+        copy_ref = {"bytes_per_copy": 2 << 30, "avg_ms": round(copy_ms, 4),
+                    "achieved": round((2 << 30) / (copy_ms * 1e-3) / 1e9, 2)}
+        del src, dst
+        log("reference copy: %.4f ms" % copy_ms)
 
     # ---------------- derived figures --------------------------------------
     D, H = dp.K, dp.H
@@ -274,6 +312,10 @@ def main(argv=None):
             "traffic": traffic,
             "algorithmic_bytes_per_launch": dec_bytes,
             "avg_launch_ms": round(dec_avg, 5),
+            "median_launch_ms": round(dec_med, 5),
+            "copy_reference": copy_ref,
+            "vs_copy": None if copy_ref is None else
+                round(dec_gbps / copy_ref["achieved"], 4),
             "back_to_back": None if b2b_ms is None else {
                 "launches": n_b2b,
                 "avg_launch_ms": round(b2b_ms, 5),
@@ -285,6 +327,9 @@ def main(argv=None):
         "prefill": {
             "tokens_per_s": round(total / pre_s, 1),
             "ms": round(pre_avg, 4),
+            "median_ms": round(pre_med, 4),
+            "ckpt_every": args.ckpt_every or None,
+            "ckpt_slots": None if ck is None else int(ck.shape[0]),
             "unit": "tokens/s",
             "pages_flops": pre_flops,
             "tflops": round(pre_flops / pre_s / 1e12, 2),

@@ -143,6 +143,36 @@ kda_status_t kda_prefill_varlen(const void* q, const void* k, const void* v,
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * kda_prefill_varlen that also stores the recurrent state at a fixed token
+ * interval inside every sequence ("Kimi K3: The Manos, The Mythos, The
+ * Legendos", section "KDA prefix cache management": since the longest shared
+ * prefix is not known in advance, the fixed-size state is saved at a coarse
+ * interval, such as every 32K tokens, and at prompt boundaries, so that a
+ * later request sharing a prefix resumes from the nearest saved state; the
+ * prompt-boundary state is final_state).
+ *   ckpt_every    interval in tokens, a positive multiple of C
+ *   ckpt_states   [total_T / ckpt_every, H, Dk, Dv] fp32 (integer division).
+ *                 The state after the first j * ckpt_every tokens of sequence
+ *                 n (j >= 1, j * ckpt_every <= its length) is written to slot
+ *                 (cu_seqlens[n] + j * ckpt_every) / ckpt_every - 1.  Slots
+ *                 increase with the checkpoint's packed position, so
+ *                 distinct checkpoints never share one; slots that no
+ *                 checkpoint maps to are left untouched.  May be NULL when
+ *                 total_T < ckpt_every.
+ *   ckpt_bytes    size of the ckpt_states buffer in bytes
+ * All other arguments, and every error, as kda_prefill_varlen;
+ * ckpt_every <= 0 or not a multiple of C, or a ckpt_states buffer that is
+ * too small or misaligned, returns KDA_ERR_INVALID_ARG.
+ */
+kda_status_t kda_prefill_varlen_ckpt(
+    const void* q, const void* k, const void* v, const float* g,
+    const float* beta, const int32_t* cu_seqlens, int32_t N, int64_t total_T,
+    int32_t max_seqlen, const float* initial_state, float* final_state,
+    void* o, int32_t H, int32_t Dk, int32_t Dv, int32_t C, float scale,
+    int32_t dtype, int32_t ckpt_every, float* ckpt_states, size_t ckpt_bytes,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One decode token for each of B sequences ("FlashKDA algorithm": decode
  * follows the per-token form; "Complexity analysis": the fp32 state read and
  * write dominate, about 8*Dk*Dv bytes per head).  The state is read once and

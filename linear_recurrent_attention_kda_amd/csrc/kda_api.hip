@@ -67,6 +67,60 @@ kda_status_t check_tensors(int64_t tokens, const void* q, const void* k,
   return KDA_OK;
 }
 
+// Varlen prefill, with state checkpoints when want_ckpt.
+kda_status_t prefill_varlen(const void* q, const void* k, const void* v,
+                            const float* g, const float* beta,
+                            const int32_t* cu_seqlens, int32_t N,
+                            int64_t total_T, int32_t max_seqlen,
+                            const float* initial_state, float* final_state,
+                            void* o, int32_t H, int32_t Dk, int32_t Dv,
+                            int32_t C, float scale, int32_t dtype,
+                            bool want_ckpt, int32_t ckpt_every,
+                            float* ckpt_states, size_t ckpt_bytes,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (N <= 0 || total_T < 0 || max_seqlen < 0) return KDA_ERR_INVALID_ARG;
+  if (total_T > 0 && max_seqlen == 0) return KDA_ERR_INVALID_ARG;
+  kda_status_t st = check_prefill_common(H, Dk, Dv, C, dtype);
+  if (st != KDA_OK) return st;
+  if (N > 65535) return KDA_ERR_UNSUPPORTED;
+  if (!cu_seqlens || !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARG;
+  st = check_tensors(total_T, q, k, v, g, beta, o);
+  if (st != KDA_OK) return st;
+  if ((initial_state && !aligned(initial_state, 16)) ||
+      (final_state && !aligned(final_state, 16)))
+    return KDA_ERR_INVALID_ARG;
+  if ((int64_t)(Dv / 16) * H * N > INT_MAX)
+    return KDA_ERR_UNSUPPORTED;
+  const int64_t maxlen = max_seqlen < total_T ? max_seqlen : total_T;
+  if (want_ckpt) {
+    if (ckpt_every <= 0 || ckpt_every % C != 0) return KDA_ERR_INVALID_ARG;
+    const int64_t slots = total_T / ckpt_every;
+    if (slots > 0) {
+      if (!ckpt_states || !aligned(ckpt_states, 16)) return KDA_ERR_INVALID_ARG;
+      const double need = (double)slots * H * Dk * Dv * 4.0;
+      if (need > 9.0e18 || (double)ckpt_bytes < need) return KDA_ERR_INVALID_ARG;
+    }
+  }
+
+  kda::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.cu_seqlens = cu_seqlens;
+  a.T_fixed = 0;
+  a.N = N;
+  a.total_T = total_T;
+  a.max_chunks = (int32_t)((maxlen + C - 1) / C);
+  a.initial_state = initial_state;
+  a.final_state = final_state;
+  a.o = o;
+  a.H = H;
+  a.scale = scale;
+  a.ckpt_every = want_ckpt ? ckpt_every : 0;
+  a.ckpt_states =
+      (want_ckpt && total_T / ckpt_every > 0) ? ckpt_states : nullptr;
+  return run_prefill(a, Dk, C, dtype, workspace, workspace_bytes, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -139,34 +193,23 @@ kda_status_t kda_prefill_varlen(const void* q, const void* k, const void* v,
                                 int32_t Dk, int32_t Dv, int32_t C, float scale,
                                 int32_t dtype, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  if (N <= 0 || total_T < 0 || max_seqlen < 0) return KDA_ERR_INVALID_ARG;
-  if (total_T > 0 && max_seqlen == 0) return KDA_ERR_INVALID_ARG;
-  kda_status_t st = check_prefill_common(H, Dk, Dv, C, dtype);
-  if (st != KDA_OK) return st;
-  if (N > 65535) return KDA_ERR_UNSUPPORTED;
-  if (!cu_seqlens || !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARG;
-  st = check_tensors(total_T, q, k, v, g, beta, o);
-  if (st != KDA_OK) return st;
-  if ((initial_state && !aligned(initial_state, 16)) ||
-      (final_state && !aligned(final_state, 16)))
-    return KDA_ERR_INVALID_ARG;
-  if ((int64_t)(Dv / 16) * H * N > INT_MAX)
-    return KDA_ERR_UNSUPPORTED;
-  const int64_t maxlen = max_seqlen < total_T ? max_seqlen : total_T;
+  return prefill_varlen(q, k, v, g, beta, cu_seqlens, N, total_T, max_seqlen,
+                        initial_state, final_state, o, H, Dk, Dv, C, scale,
+                        dtype, false, 0, nullptr, 0, workspace,
+                        workspace_bytes, stream);
+}
 
-  kda::PrefillArgs a{};
-  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
-  a.cu_seqlens = cu_seqlens;
-  a.T_fixed = 0;
-  a.N = N;
-  a.total_T = total_T;
-  a.max_chunks = (int32_t)((maxlen + C - 1) / C);
-  a.initial_state = initial_state;
-  a.final_state = final_state;
-  a.o = o;
-  a.H = H;
-  a.scale = scale;
-  return run_prefill(a, Dk, C, dtype, workspace, workspace_bytes, stream);
+kda_status_t kda_prefill_varlen_ckpt(
+    const void* q, const void* k, const void* v, const float* g,
+    const float* beta, const int32_t* cu_seqlens, int32_t N, int64_t total_T,
+    int32_t max_seqlen, const float* initial_state, float* final_state,
+    void* o, int32_t H, int32_t Dk, int32_t Dv, int32_t C, float scale,
+    int32_t dtype, int32_t ckpt_every, float* ckpt_states, size_t ckpt_bytes,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_varlen(q, k, v, g, beta, cu_seqlens, N, total_T, max_seqlen,
+                        initial_state, final_state, o, H, Dk, Dv, C, scale,
+                        dtype, true, ckpt_every, ckpt_states, ckpt_bytes,
+                        workspace, workspace_bytes, stream);
 }
 
 kda_status_t kda_decode_step(const void* q, const void* k, const void* v,

@@ -79,6 +79,8 @@ struct PrefillArgs {
   float scale;
   char* ws;
   int64_t nslots;
+  float* ckpt_states;          // state checkpoints, or nullptr
+  int32_t ckpt_every;          // checkpoint interval in tokens (multiple of C)
 };
 
 struct DecodeArgs {

@@ -41,7 +41,7 @@ struct ChunkOps {
   float4 gm[NCT];                 // gamma for the 4 state rows of the lane
 };
 
-template <typename Tout, int D, int C, int BV, int PF, int NW>
+template <typename Tout, int D, int C, int BV, int PF, int NW, bool kCkpt>
 __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
   constexpr int K = D, V = D;
   constexpr int NVT = V / BV;              // d_v slices per head
@@ -302,6 +302,27 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
         *reinterpret_cast<bf16x4*>(&s_SbT[16 * jt + rl][16 * ct + 4 * kg]) = sb;
       }
     }
+    // state checkpoint after this chunk: "Kimi K3: The Manos, The Mythos,
+    // The Legendos", section "KDA prefix cache management" (the state saved
+    // every so many tokens).  The condition is uniform over the workgroup.
+    if (kCkpt) {
+      const int64_t p = (ci + 1) * C;  // tokens of the sequence done
+      if (p % a.ckpt_every == 0 && p <= eos - bos) {
+        const int64_t cslot = (bos + p) / a.ckpt_every - 1;
+        float* dst = a.ckpt_states + ((size_t)cslot * H + h) * (size_t)K * V;
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+          const int t = s0t + i;
+          if (kAllS || t < NST) {
+            const int ct = t / JT, jt = t % JT;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              dst[(size_t)(16 * ct + 4 * kg + e) * V + j0 + 16 * jt + rl] =
+                  S[i][e];
+          }
+        }
+      }
+    }
     load_s(op, nb);
   };
 
@@ -356,11 +377,12 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
   }
 }
 
-template <typename Tout, int D, int C, int BV, int PF, int NW>
+template <typename Tout, int D, int C, int BV, int PF, int NW,
+          bool kCkpt = false>
 hipError_t launch_bv(const PrefillArgs& a, hipStream_t st) {
   const unsigned blocks = (unsigned)(D / BV) * (unsigned)a.H * (unsigned)a.N;
-  return launch_kernel(recur_kernel<Tout, D, C, BV, PF, NW>, dim3(blocks),
-                       dim3(64 * NW), st, a);
+  return launch_kernel(recur_kernel<Tout, D, C, BV, PF, NW, kCkpt>,
+                       dim3(blocks), dim3(64 * NW), st, a);
 }
 
 // Slice width.  Wider slices re-read the per-chunk tensors fewer times and
@@ -408,6 +430,8 @@ inline int pick_waves() {
 
 template <typename Tout, int D, int C, int BV>
 hipError_t launch_w(const PrefillArgs& a, hipStream_t st) {
+  // state checkpoints: their own kernel variant, default shape
+  if (a.ckpt_states) return launch_bv<Tout, D, C, BV, 2, 4, true>(a, st);
   const int pf = pick_pf();
   if (pick_waves() == 8 && (D / 16) * (BV / 16) >= 8 && (C / 16) * (BV / 16) >= 8)
     return pf == 2 ? launch_bv<Tout, D, C, BV, 2, 8>(a, st)

@@ -63,6 +63,10 @@ def load() -> ctypes.CDLL:
         lib.kda_prefill_varlen.argtypes = [
             vp, vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, i32,
             i32, f32, i32, vp, sz, vp]
+        lib.kda_prefill_varlen_ckpt.restype = i32
+        lib.kda_prefill_varlen_ckpt.argtypes = [
+            vp, vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, i32,
+            i32, f32, i32, i32, vp, sz, vp, sz, vp]
         lib.kda_decode_step.restype = i32
         lib.kda_decode_step.argtypes = [
             vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
@@ -214,6 +218,77 @@ def kda_prefill_varlen(q, k, v, g, beta, cu_seqlens, max_seqlen: int,
     if st != KDA_OK:
         raise KDAError("kda_prefill_varlen", st)
     return o, final_state
+
+
+def kda_prefill_varlen_ckpt(q, k, v, g, beta, cu_seqlens, max_seqlen: int,
+                            initial_state=None, *, ckpt_every: int,
+                            chunk_size: int = 64, scale: float = 1.0,
+                            output_final_state: bool = True, final_state=None,
+                            o=None, ckpt_states=None, workspace=None):
+    """kda_prefill_varlen that also stores the state every `ckpt_every`
+    tokens (a multiple of chunk_size) inside each sequence.
+
+    Returns (o, final_state, ckpt_states) with ckpt_states
+    [total_T // ckpt_every, H, Dk, Dv] fp32: the state after the first
+    j * ckpt_every tokens of sequence n sits in slot
+    (cu_seqlens[n] + j * ckpt_every) // ckpt_every - 1 (see
+    `kda_ckpt_slots`); other slots are left as allocated.
+    """
+    lib = load()
+    total_T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    N = cu_seqlens.numel() - 1
+    for t, n, s, dt in ((q, "q", (total_T, H, Dk), q.dtype),
+                        (k, "k", (total_T, H, Dk), q.dtype),
+                        (v, "v", (total_T, H, Dv), q.dtype),
+                        (g, "g", (total_T, H, Dk), torch.float32),
+                        (beta, "beta", (total_T, H), torch.float32),
+                        (cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)):
+        _check(t, n, s, dt, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (N, H, Dk, Dv), torch.float32,
+               dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32,
+                                  device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (N, H, Dk, Dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((total_T, H, Dv), dtype=q.dtype, device=dev)
+    _check(o, "o", (total_T, H, Dv), q.dtype, dev)
+    if ckpt_every <= 0:
+        raise ValueError("ckpt_every must be positive")
+    slots = total_T // ckpt_every
+    if ckpt_states is None:
+        ckpt_states = torch.zeros((slots, H, Dk, Dv), dtype=torch.float32,
+                                  device=dev)
+    _check(ckpt_states, "ckpt_states", (slots, H, Dk, Dv), torch.float32, dev)
+    if workspace is None:
+        workspace = workspace_for(N, total_T, H, Dk, Dv, chunk_size, dev)
+    st = lib.kda_prefill_varlen_ckpt(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N,
+        total_T, int(max_seqlen), _ptr(initial_state), _ptr(final_state),
+        _ptr(o), H, Dk, Dv, chunk_size, scale, _dtype_code(q),
+        int(ckpt_every), _ptr(ckpt_states) if slots > 0 else None,
+        ckpt_states.numel() * 4, _ptr(workspace), workspace.numel(),
+        _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_prefill_varlen_ckpt", st)
+    return o, final_state, ckpt_states
+
+
+def kda_ckpt_slots(cu_seqlens, ckpt_every: int):
+    """Host-side map of the checkpoints kda_prefill_varlen_ckpt writes:
+    a list of (sequence n, tokens done p, slot), p = j * ckpt_every."""
+    cu = [int(x) for x in cu_seqlens]
+    out = []
+    for n in range(len(cu) - 1):
+        p = ckpt_every
+        while p <= cu[n + 1] - cu[n]:
+            out.append((n, p, (cu[n] + p) // ckpt_every - 1))
+            p += ckpt_every
+    return out
 
 
 def kda_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, o=None):

@@ -23,7 +23,8 @@ def test_exports_every_declared_symbol():
     names = kda.declared_functions()
     assert set(names) == {"kda_abi_version", "kda_status_string",
                           "kda_prefill_workspace_size", "kda_prefill_chunked",
-                          "kda_prefill_varlen", "kda_decode_step"}
+                          "kda_prefill_varlen", "kda_prefill_varlen_ckpt",
+                          "kda_decode_step"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -122,3 +123,32 @@ def test_prefill_varlen_validation():
     assert _varlen(lib, C=8) == UNSUP
     assert _varlen(lib, ws_bytes=10) == WS
     assert _varlen(lib, v=NULL) == INVALID
+
+
+def _ckpt(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, cu=P, N=2, total=300, maxlen=200,
+             s0=NULL, s1=NULL, o=P, H=2, Dk=64, Dv=64, C=32, scale=1.0,
+             dtype=0, every=64, ck=P, ck_bytes=1 << 40, ws=P,
+             ws_bytes=1 << 40, stream=NULL)
+    a.update(kw)
+    return lib.kda_prefill_varlen_ckpt(
+        a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"],
+        a["total"], a["maxlen"], a["s0"], a["s1"], a["o"], a["H"], a["Dk"],
+        a["Dv"], a["C"], a["scale"], a["dtype"], a["every"], a["ck"],
+        a["ck_bytes"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_prefill_varlen_ckpt_validation():
+    """Every call here fails validation (nothing is launched)."""
+    lib = kda.load()
+    assert _ckpt(lib, every=0) == INVALID
+    assert _ckpt(lib, every=-64) == INVALID
+    assert _ckpt(lib, every=48) == INVALID           # not a multiple of C
+    assert _ckpt(lib, ck=NULL) == INVALID            # 300 // 64 = 4 slots
+    assert _ckpt(lib, ck=ctypes.c_void_p(0x100008)) == INVALID
+    # 4 slots x 2 heads x 64 x 64 x 4 B = 131072 B needed
+    assert _ckpt(lib, ck_bytes=131071) == INVALID
+    # the checks shared with kda_prefill_varlen come first
+    assert _ckpt(lib, N=0) == INVALID
+    assert _ckpt(lib, C=8, every=64) == UNSUP
+    assert _ckpt(lib, ws_bytes=10) == WS
