@@ -98,6 +98,10 @@ def main(argv=None):
                     help="run the prefill through kda_prefill_varlen_ckpt, "
                          "storing the state every N tokens (a multiple of "
                          "the chunk size)")
+    ap.add_argument("--spec-tokens", type=int, default=0,
+                    help="also time speculative verify + commit of this many "
+                         "draft tokens per sequence on the decode batch "
+                         "(outside the timed steps)")
     ap.add_argument("--step-only", action="store_true",
                     help="skip the measurements taken after the timed steps "
                          "(back-to-back decode, reference copy), so that a "
@@ -262,6 +266,10 @@ def main(argv=None):
         del src, dst
         log("reference copy: %.4f ms" % copy_ms)
 
+    spec = None
+    if args.spec_tokens and not args.step_only:
+        spec = time_spec(args.spec_tokens, dp, states, dev, stream, ev)
+
     # ---------------- derived figures --------------------------------------
     D, H = dp.K, dp.H
     dec_bytes = counts.decode_bytes_per_head(D) * dp.B * H
@@ -351,11 +359,67 @@ def main(argv=None):
         },
     }
 
+    if spec is not None:
+        result["spec"] = spec
+
     # ---------------- CPU baseline: the oracle on the host cores -----------
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(dp, pp)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def time_spec(T, dp, states, dev, stream, ev):
+    """Speculative verify of T draft tokens per sequence on the decode
+    batch, then commit of all T, against T single decode steps."""
+    import torch
+    from linear_recurrent_attention_kda_amd import kda
+    sp = inputs.make("varlen", seed=5, H=dp.H, K=dp.K, V=dp.V,
+                     lengths=[T] * dp.B)
+    B, H = dp.B, dp.H
+    shp = lambda x: torch.from_numpy(  # noqa: E731
+        np.ascontiguousarray(x.reshape((B, T) + x.shape[1:]))).to(dev)
+    q, k, v = (shp(x).to(torch.bfloat16) for x in (sp.q, sp.k, sp.v))
+    g, beta = shp(sp.g), shp(sp.beta)
+    o = torch.empty((B, T, H, dp.V), dtype=torch.bfloat16, device=dev)
+    u = torch.empty((B, T, H, dp.V), dtype=torch.float32, device=dev)
+    acc = torch.full((B,), T, dtype=torch.int32, device=dev)
+    qs, ks, vs, gs, bs = ([x[:, t].contiguous() for t in range(T)]
+                          for x in (q, k, v, g, beta))
+    od = torch.empty((B, H, dp.V), dtype=torch.bfloat16, device=dev)
+    n = 20
+    rec = []
+    for i in range(n + 3):
+        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+        st = states[i % 3]
+        e0.record(stream)
+        kda.kda_spec_verify(q, k, v, g, beta, st, o=o, u=u)
+        e1.record(stream)
+        kda.kda_spec_commit(k, g, u, acc, st)
+        e2.record(stream)
+        for t in range(T):
+            kda.kda_decode_step(qs[t], ks[t], vs[t], gs[t], bs[t],
+                                states[(i + 1) % 3], o=od)
+        e3.record(stream)
+        rec.append((e0, e1, e2, e3))
+    torch.cuda.synchronize()
+    rec = rec[3:]
+    ver = float(np.mean([a.elapsed_time(b) for a, b, _, _ in rec]))
+    com = float(np.mean([b.elapsed_time(c) for _, b, c, _ in rec]))
+    dec = float(np.mean([c.elapsed_time(d) for _, _, c, d in rec]))
+    per_head = dp.K * dp.V * 4
+    log("spec T=%d: verify %.4f ms, commit %.4f ms, %d decode steps %.4f ms"
+        % (T, ver, com, T, dec))
+    return {
+        "draft_tokens": T, "sequences": B, "heads": H,
+        "verify_ms": round(ver, 5), "commit_ms": round(com, 5),
+        "verify_commit_ms": round(ver + com, 5),
+        "decode_steps_ms": round(dec, 5),
+        "verify_state_gbps": round(B * H * per_head / (ver * 1e-3) / 1e9, 1),
+        "commit_state_gbps": round(2 * B * H * per_head / (com * 1e-3) / 1e9,
+                                   1),
+        "speedup_vs_decode_steps": round(dec / (ver + com), 3),
+    }
 
 
 def cpu_baseline(dp, pp):

@@ -188,6 +188,42 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v,
                              int32_t Dv, float scale, int32_t dtype,
                              void* stream);
 
+/*
+ * Speculative-decode verify ("Model evolution after DeepSeek V3",
+ * uncledou.site, section four: a cheap draft proposes several tokens and the
+ * large model checks them in one parallel pass).  Runs T draft tokens of each
+ * of B sequences through the recurrence from `state`, in order, exactly as T
+ * decode steps would, and writes every position's output and the fp32
+ * pseudo-values u_t = beta_t (v_t - (Diag(exp g_t) S_{t-1})^T k_t).  The
+ * state itself is NOT modified: call kda_spec_commit with the number of
+ * accepted tokens afterwards.
+ *   q, k [B, T, H, Dk] dtype; v [B, T, H, Dv] dtype; g [B, T, H, Dk] fp32;
+ *   beta [B, T, H] fp32; state [B, H, Dk, Dv] fp32 (read only);
+ *   o [B, T, H, Dv] dtype (written); u [B, T, H, Dv] fp32 (written).
+ * B, H >= 1; 1 <= T <= 16 (larger T returns KDA_ERR_UNSUPPORTED).
+ */
+kda_status_t kda_spec_verify(const void* q, const void* k, const void* v,
+                             const float* g, const float* beta,
+                             const float* state, void* o, float* u, int32_t B,
+                             int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                             float scale, int32_t dtype, void* stream);
+
+/*
+ * Advance `state` by the first accepted[b] draft tokens of sequence b, using
+ * the k, g of those tokens and the u that kda_spec_verify wrote for them
+ * (S <- Diag(exp g_t) S + k_t u_t^T for t < accepted[b]).  The result equals
+ * accepted[b] decode steps.  accepted is a DEVICE int32 array [B], read by
+ * the kernel (no host synchronisation); values are clamped to [0, T], and a
+ * sequence with 0 accepted tokens keeps its state untouched.
+ *   k [B, T, H, Dk] dtype; g [B, T, H, Dk] fp32; u [B, T, H, Dv] fp32;
+ *   state [B, H, Dk, Dv] fp32, updated in place.
+ * Arguments as kda_spec_verify; dtype is that of k.
+ */
+kda_status_t kda_spec_commit(const void* k, const float* g, const float* u,
+                             const int32_t* accepted, float* state, int32_t B,
+                             int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                             int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -239,4 +239,60 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v,
   return KDA_OK;
 }
 
+kda_status_t kda_spec_verify(const void* q, const void* k, const void* v,
+                             const float* g, const float* beta,
+                             const float* state, void* o, float* u, int32_t B,
+                             int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                             float scale, int32_t dtype, void* stream) {
+  if (B <= 0 || H <= 0 || T <= 0 || Dk <= 0 || Dv <= 0)
+    return KDA_ERR_INVALID_ARG;
+  if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_FP32)
+    return KDA_ERR_UNSUPPORTED;
+  if (!supported_dims(Dk, Dv) || T > kda::max_spec_tokens())
+    return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > INT_MAX) return KDA_ERR_UNSUPPORTED;
+  kda_status_t st = check_tensors((int64_t)B * T, q, k, v, g, beta, o);
+  if (st != KDA_OK) return st;
+  if (!state || !aligned(state, 16) || !u || !aligned(u, 16))
+    return KDA_ERR_INVALID_ARG;
+  kda::SpecArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.state = const_cast<float*>(state);
+  a.o = o;
+  a.u = u;
+  a.B = B; a.T = T; a.H = H;
+  a.scale = scale;
+  if (kda::launch_spec(a, Dk, dtype == KDA_DTYPE_BF16, false,
+                       static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KDA_ERR_LAUNCH;
+  return KDA_OK;
+}
+
+kda_status_t kda_spec_commit(const void* k, const float* g, const float* u,
+                             const int32_t* accepted, float* state, int32_t B,
+                             int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                             int32_t dtype, void* stream) {
+  if (B <= 0 || H <= 0 || T <= 0 || Dk <= 0 || Dv <= 0)
+    return KDA_ERR_INVALID_ARG;
+  if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_FP32)
+    return KDA_ERR_UNSUPPORTED;
+  if (!supported_dims(Dk, Dv) || T > kda::max_spec_tokens())
+    return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > INT_MAX) return KDA_ERR_UNSUPPORTED;
+  if (!k || !g || !u || !accepted || !state) return KDA_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(g, 16) || !aligned(u, 16) ||
+      !aligned(state, 16) || !aligned(accepted, 4))
+    return KDA_ERR_INVALID_ARG;
+  kda::SpecArgs a{};
+  a.k = k; a.g = g;
+  a.u = const_cast<float*>(u);
+  a.accepted = accepted;
+  a.state = state;
+  a.B = B; a.T = T; a.H = H;
+  if (kda::launch_spec(a, Dk, dtype == KDA_DTYPE_BF16, true,
+                       static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KDA_ERR_LAUNCH;
+  return KDA_OK;
+}
+
 }  // extern "C"

@@ -83,6 +83,17 @@ struct PrefillArgs {
   int32_t ckpt_every;          // checkpoint interval in tokens (multiple of C)
 };
 
+struct SpecArgs {
+  const void* q; const void* k; const void* v;   // [B, T, H, D]
+  const float* g; const float* beta;             // [B, T, H, D], [B, T, H]
+  float* state;                                  // [B, H, D, D]
+  void* o;                                       // [B, T, H, D] (verify)
+  float* u;                                      // [B, T, H, D] fp32
+  const int32_t* accepted;                       // [B] (commit)
+  int32_t B, T, H;
+  float scale;
+};
+
 struct DecodeArgs {
   const void* q; const void* k; const void* v;
   const float* g; const float* beta;
@@ -108,5 +119,8 @@ hipError_t launch_prep(const PrefillArgs& a, int D, int C, bool bf16_io,
                        hipStream_t s);
 hipError_t launch_recur(const PrefillArgs& a, int D, int C, bool bf16_io,
                         hipStream_t s);
+hipError_t launch_spec(const SpecArgs& a, int D, bool bf16_io, bool commit,
+                       hipStream_t s);
+int max_spec_tokens();
 
 }  // namespace kda

@@ -1,0 +1,236 @@
+// Speculative-decode verify and commit.
+//
+// "Model evolution after DeepSeek V3" (uncledou.site), section four
+// (speculative sampling has become standard): decode is bound by memory
+// bandwidth, so a cheap draft proposes several tokens, the large model
+// checks them in one parallel pass and keeps the ones it agrees with.  For a
+// KDA layer this means running T draft tokens through the recurrence from a
+// cached state, emitting every draft position's output, and afterwards
+// advancing the state by only the accepted prefix.
+//
+// verify: per (sequence, head), the fp32 state is read once into registers
+//   and the T tokens are applied in order, exactly as the decode kernel
+//   applies one token:
+//     aS = Diag(exp g_t) S;  x = (aS)^T k_t;  y = (aS)^T q_t
+//     u_t = beta_t (v_t - x);  o_t = scale (y + (q_t . k_t) u_t)
+//     S = aS + k_t u_t^T
+//   o_t and the fp32 pseudo-values u_t are written; the state in memory is
+//   left unchanged, so rejecting any suffix costs nothing.
+// commit: per (sequence, head), with a = accepted[sequence] (clamped to
+//   [0, T]) the state is read once, the a updates S = Diag(exp g_t) S +
+//   k_t u_t^T are applied with the decode kernel's arithmetic, and the state
+//   is written once (not at all when a = 0).
+// State traffic per head: verify reads 4 d^2 bytes and commit reads and
+// writes 8 d^2, against 8 d^2 per accepted token for single decode steps.
+#include <stdlib.h>
+
+#include "kda_device.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int kMaxSpecT = 16;
+
+// Thread (rg, cg) owns the float4 column group cg of rows rg, rg + RG, ...
+// (the decode kernel's mapping); a wave holds 64 / CG lanes of each column
+// group.
+template <int D, int NT>
+struct SpecTiling {
+  static constexpr int CG = D / 4;
+  static constexpr int RG = NT / CG;
+  static constexpr int RPT = D / RG;
+  static constexpr int NW = NT / 64;
+  static_assert(NT % CG == 0 && D % RG == 0 && 32 % CG == 0 && NT >= 64,
+                "spec tiling");
+};
+
+template <typename Tio, int D, int NT>
+__global__ __launch_bounds__(NT) void spec_verify_kernel(SpecArgs a) {
+  using Ti = SpecTiling<D, NT>;
+  constexpr int CG = Ti::CG, RG = Ti::RG, RPT = Ti::RPT, NW = Ti::NW;
+  __shared__ float s_alpha[kMaxSpecT][D], s_k[kMaxSpecT][D], s_q[kMaxSpecT][D];
+  __shared__ float4 s_red[2][NW][CG][3];
+
+  const int bh = blockIdx.x;
+  const int b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x;
+  const int cg = tid % CG, rg = tid / CG;
+  const int T = a.T;
+  const float* S = a.state + (size_t)bh * D * D;
+
+  float4 s[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+    s[i] = *reinterpret_cast<const float4*>(S + (size_t)(rg + RG * i) * D +
+                                            4 * cg);
+
+  // token t of sequence b, head h: row (b * T + t) * H + h
+  for (int e = tid; e < T * D; e += NT) {
+    const int t = e / D, c = e % D;
+    const size_t row = ((size_t)b * T + t) * a.H + h;
+    s_alpha[t][c] = __builtin_amdgcn_exp2f(a.g[row * D + c] * kLog2e);
+    s_k[t][c] = io<Tio>::to_f(static_cast<const Tio*>(a.k)[row * D + c]);
+    s_q[t][c] = io<Tio>::to_f(static_cast<const Tio*>(a.q)[row * D + c]);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < T; ++t) {
+    float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
+    float qk = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int c = rg + RG * i;
+      const float al = s_alpha[t][c], kc = s_k[t][c], qc = s_q[t][c];
+      s[i].x *= al; s[i].y *= al; s[i].z *= al; s[i].w *= al;
+      x[0] += s[i].x * kc; x[1] += s[i].y * kc; x[2] += s[i].z * kc; x[3] += s[i].w * kc;
+      y[0] += s[i].x * qc; y[1] += s[i].y * qc; y[2] += s[i].z * qc; y[3] += s[i].w * qc;
+      qk += qc * kc;
+    }
+#pragma unroll
+    for (int off = 32; off >= CG; off >>= 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] += __shfl_xor(x[j], off);
+        y[j] += __shfl_xor(y[j], off);
+      }
+      qk += __shfl_xor(qk, off);
+    }
+    // double-buffered by token parity: one barrier per token
+    float4 (*red)[CG][3] = s_red[t & 1];
+    if ((tid & 63) < CG) {
+      const int w = tid / 64;
+      red[w][cg][0] = make_float4(x[0], x[1], x[2], x[3]);
+      red[w][cg][1] = make_float4(y[0], y[1], y[2], y[3]);
+      red[w][cg][2] = make_float4(qk, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+    float4 X = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 Y = make_float4(0.f, 0.f, 0.f, 0.f);
+    float QK = 0.f;
+#pragma unroll
+    for (int r = 0; r < NW; ++r) {
+      const float4 xr = red[r][cg][0], yr = red[r][cg][1];
+      X.x += xr.x; X.y += xr.y; X.z += xr.z; X.w += xr.w;
+      Y.x += yr.x; Y.y += yr.y; Y.z += yr.z; Y.w += yr.w;
+      QK += red[r][cg][2].x;
+    }
+    const size_t row = ((size_t)b * T + t) * a.H + h;
+    const Tio* v = static_cast<const Tio*>(a.v) + row * D + 4 * cg;
+    const float beta = a.beta[row];
+    float4 u;
+    u.x = beta * (io<Tio>::to_f(v[0]) - X.x);
+    u.y = beta * (io<Tio>::to_f(v[1]) - X.y);
+    u.z = beta * (io<Tio>::to_f(v[2]) - X.z);
+    u.w = beta * (io<Tio>::to_f(v[3]) - X.w);
+    if (rg == 0) {
+      Tio* o = static_cast<Tio*>(a.o) + row * D + 4 * cg;
+      o[0] = io<Tio>::from_f(a.scale * (Y.x + QK * u.x));
+      o[1] = io<Tio>::from_f(a.scale * (Y.y + QK * u.y));
+      o[2] = io<Tio>::from_f(a.scale * (Y.z + QK * u.z));
+      o[3] = io<Tio>::from_f(a.scale * (Y.w + QK * u.w));
+      *reinterpret_cast<float4*>(a.u + row * D + 4 * cg) = u;
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const float kc = s_k[t][rg + RG * i];
+      s[i].x = s[i].x + kc * u.x; s[i].y = s[i].y + kc * u.y;
+      s[i].z = s[i].z + kc * u.z; s[i].w = s[i].w + kc * u.w;
+    }
+  }
+}
+
+template <typename Tio, int D, int NT>
+__global__ __launch_bounds__(NT) void spec_commit_kernel(SpecArgs a) {
+  using Ti = SpecTiling<D, NT>;
+  constexpr int CG = Ti::CG, RG = Ti::RG, RPT = Ti::RPT;
+  __shared__ float s_alpha[kMaxSpecT][D], s_k[kMaxSpecT][D];
+
+  const int bh = blockIdx.x;
+  const int b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x;
+  const int cg = tid % CG, rg = tid / CG;
+  const int T = a.T;
+  int acc = a.accepted[b];
+  acc = acc < 0 ? 0 : (acc > T ? T : acc);
+  if (acc == 0) return;  // uniform: the state stays as it is
+
+  float* S = a.state + (size_t)bh * D * D;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, D * D * 4);
+  float4 s[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+    s[i] = __builtin_bit_cast(
+        float4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, ((rg + RG * i) * D + 4 * cg) * 4, 0, kCachePolicyNt));
+  for (int e = tid; e < acc * D; e += NT) {
+    const int t = e / D, c = e % D;
+    const size_t row = ((size_t)b * T + t) * a.H + h;
+    s_alpha[t][c] = __builtin_amdgcn_exp2f(a.g[row * D + c] * kLog2e);
+    s_k[t][c] = io<Tio>::to_f(static_cast<const Tio*>(a.k)[row * D + c]);
+  }
+  __syncthreads();
+  for (int t = 0; t < acc; ++t) {
+    const size_t row = ((size_t)b * T + t) * a.H + h;
+    const float4 u = *reinterpret_cast<const float4*>(a.u + row * D + 4 * cg);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int c = rg + RG * i;
+      const float al = s_alpha[t][c], kc = s_k[t][c];
+      s[i].x *= al; s[i].y *= al; s[i].z *= al; s[i].w *= al;
+      s[i].x = s[i].x + kc * u.x; s[i].y = s[i].y + kc * u.y;
+      s[i].z = s[i].z + kc * u.z; s[i].w = s[i].w + kc * u.w;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+    __builtin_amdgcn_raw_buffer_store_b128(
+        __builtin_bit_cast(u32x4, s[i]), rs, ((rg + RG * i) * D + 4 * cg) * 4,
+        0, kCachePolicyNt);
+}
+
+// Threads per workgroup, capped by D^2 / 4.  Commit streams the state like
+// the decode kernel (1024 threads at D = 128).  Verify reduces across the
+// waves once per token, and every thread reads every wave's partial sums, so
+// it uses 4 waves (256 threads, 16 rows per thread at D = 128): a sixth of
+// the LDS traffic per token of 16 waves, and four workgroups per CU.
+template <int D, int CAP>
+constexpr int spec_threads() {
+  return (D * D / 4) < CAP ? (D * D / 4) : CAP;
+}
+
+template <typename Tio, int D>
+hipError_t launch_d(const SpecArgs& a, bool commit, hipStream_t st) {
+  const unsigned blocks = (unsigned)a.B * (unsigned)a.H;
+  if (commit) {
+    constexpr int NT = spec_threads<D, 1024>();
+    return launch_kernel(spec_commit_kernel<Tio, D, NT>, dim3(blocks),
+                         dim3(NT), st, a);
+  }
+  constexpr int NT = spec_threads<D, 256>();
+  return launch_kernel(spec_verify_kernel<Tio, D, NT>, dim3(blocks), dim3(NT),
+                       st, a);
+}
+
+template <typename Tio>
+hipError_t launch_t(const SpecArgs& a, int D, bool commit, hipStream_t st) {
+  switch (D) {
+    case 16: return launch_d<Tio, 16>(a, commit, st);
+    case 32: return launch_d<Tio, 32>(a, commit, st);
+    case 64: return launch_d<Tio, 64>(a, commit, st);
+    case 128: return launch_d<Tio, 128>(a, commit, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int max_spec_tokens() { return kMaxSpecT; }
+
+hipError_t launch_spec(const SpecArgs& a, int D, bool bf16_io, bool commit,
+                       hipStream_t st) {
+  return bf16_io ? launch_t<bf16>(a, D, commit, st)
+                 : launch_t<float>(a, D, commit, st);
+}
+
+}  // namespace kda

@@ -67,6 +67,13 @@ def load() -> ctypes.CDLL:
         lib.kda_prefill_varlen_ckpt.argtypes = [
             vp, vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, i32,
             i32, f32, i32, i32, vp, sz, vp, sz, vp]
+        lib.kda_spec_verify.restype = i32
+        lib.kda_spec_verify.argtypes = [
+            vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
+            vp]
+        lib.kda_spec_commit.restype = i32
+        lib.kda_spec_commit.argtypes = [
+            vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
         lib.kda_decode_step.restype = i32
         lib.kda_decode_step.argtypes = [
             vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
@@ -315,3 +322,57 @@ def kda_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, o=None):
     if st != KDA_OK:
         raise KDAError("kda_decode_step", st)
     return o
+
+
+def kda_spec_verify(q, k, v, g, beta, state, *, scale: float = 1.0, o=None,
+                    u=None):
+    """Run T draft tokens per sequence from `state` (left unchanged).
+
+    q, k, g: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H];
+    state: [B, H, Dk, Dv] fp32.  Returns (o [B, T, H, Dv], u [B, T, H, Dv]
+    fp32), u being what kda_spec_commit needs.
+    """
+    lib = load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    for t, n, s_, dt in ((q, "q", (B, T, H, Dk), q.dtype),
+                         (k, "k", (B, T, H, Dk), q.dtype),
+                         (v, "v", (B, T, H, Dv), q.dtype),
+                         (g, "g", (B, T, H, Dk), torch.float32),
+                         (beta, "beta", (B, T, H), torch.float32),
+                         (state, "state", (B, H, Dk, Dv), torch.float32)):
+        _check(t, n, s_, dt, dev)
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev)
+    _check(o, "o", (B, T, H, Dv), q.dtype, dev)
+    if u is None:
+        u = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+    _check(u, "u", (B, T, H, Dv), torch.float32, dev)
+    st = lib.kda_spec_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(state), _ptr(o), _ptr(u), B, T, H, Dk, Dv,
+                             scale, _dtype_code(q), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_spec_verify", st)
+    return o, u
+
+
+def kda_spec_commit(k, g, u, accepted, state):
+    """Advance `state` [B, H, Dk, Dv] in place by accepted[b] (device int32
+    [B]) of the draft tokens verified with kda_spec_verify.  Returns state."""
+    lib = load()
+    B, T, H, Dk = k.shape
+    Dv = u.shape[-1]
+    dev = k.device
+    for t, n, s_, dt in ((k, "k", (B, T, H, Dk), k.dtype),
+                         (g, "g", (B, T, H, Dk), torch.float32),
+                         (u, "u", (B, T, H, Dv), torch.float32),
+                         (accepted, "accepted", (B,), torch.int32),
+                         (state, "state", (B, H, Dk, Dv), torch.float32)):
+        _check(t, n, s_, dt, dev)
+    st = lib.kda_spec_commit(_ptr(k), _ptr(g), _ptr(u), _ptr(accepted),
+                             _ptr(state), B, T, H, Dk, Dv, _dtype_code(k),
+                             _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_spec_commit", st)
+    return state

@@ -24,7 +24,8 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"kda_abi_version", "kda_status_string",
                           "kda_prefill_workspace_size", "kda_prefill_chunked",
                           "kda_prefill_varlen", "kda_prefill_varlen_ckpt",
-                          "kda_decode_step"}
+                          "kda_decode_step", "kda_spec_verify",
+                          "kda_spec_commit"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -152,3 +153,42 @@ def test_prefill_varlen_ckpt_validation():
     assert _ckpt(lib, N=0) == INVALID
     assert _ckpt(lib, C=8, every=64) == UNSUP
     assert _ckpt(lib, ws_bytes=10) == WS
+
+
+def _verify(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, state=P, o=P, u=P, B=2, T=4, H=2,
+             Dk=128, Dv=128, scale=1.0, dtype=0, stream=NULL)
+    a.update(kw)
+    return lib.kda_spec_verify(a["q"], a["k"], a["v"], a["g"], a["beta"],
+                               a["state"], a["o"], a["u"], a["B"], a["T"],
+                               a["H"], a["Dk"], a["Dv"], a["scale"],
+                               a["dtype"], a["stream"])
+
+
+def _commit(lib, **kw):
+    a = dict(k=P, g=P, u=P, acc=P, state=P, B=2, T=4, H=2, Dk=128, Dv=128,
+             dtype=0, stream=NULL)
+    a.update(kw)
+    return lib.kda_spec_commit(a["k"], a["g"], a["u"], a["acc"], a["state"],
+                               a["B"], a["T"], a["H"], a["Dk"], a["Dv"],
+                               a["dtype"], a["stream"])
+
+
+def test_spec_validation():
+    """Every call here fails validation (nothing is launched)."""
+    lib = kda.load()
+    assert _verify(lib, T=0) == INVALID
+    assert _verify(lib, T=17) == UNSUP
+    assert _verify(lib, B=0) == INVALID
+    assert _verify(lib, Dk=96, Dv=96) == UNSUP
+    assert _verify(lib, dtype=5) == UNSUP
+    assert _verify(lib, u=NULL) == INVALID
+    assert _verify(lib, state=MIS) == INVALID
+    assert _verify(lib, q=NULL) == INVALID
+    assert _commit(lib, T=0) == INVALID
+    assert _commit(lib, T=17) == UNSUP
+    assert _commit(lib, acc=NULL) == INVALID
+    assert _commit(lib, acc=ctypes.c_void_p(0x100002)) == INVALID
+    assert _commit(lib, state=NULL) == INVALID
+    assert _commit(lib, u=MIS) == INVALID
+    assert _commit(lib, Dk=64, Dv=128) == UNSUP
