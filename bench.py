@@ -102,6 +102,10 @@ def main(argv=None):
                     help="also time speculative verify + commit of this many "
                          "draft tokens per sequence on the decode batch "
                          "(outside the timed steps)")
+    ap.add_argument("--epilogue", action="store_true",
+                    help="also time the output epilogue: standalone over the "
+                         "prefill output, and fused into the decode step "
+                         "(outside the timed steps)")
     ap.add_argument("--step-only", action="store_true",
                     help="skip the measurements taken after the timed steps "
                          "(back-to-back decode, reference copy), so that a "
@@ -269,6 +273,9 @@ def main(argv=None):
     spec = None
     if args.spec_tokens and not args.step_only:
         spec = time_spec(args.spec_tokens, dp, states, dev, stream, ev)
+    epi = None
+    if args.epilogue and not args.step_only:
+        epi = time_epilogue(po, dq, dk, dv, dg, dbeta, states, dev, stream, ev)
 
     # ---------------- derived figures --------------------------------------
     D, H = dp.K, dp.H
@@ -361,6 +368,8 @@ def main(argv=None):
 
     if spec is not None:
         result["spec"] = spec
+    if epi is not None:
+        result["epilogue"] = epi
 
     # ---------------- CPU baseline: the oracle on the host cores -----------
     if not args.no_cpu_baseline:
@@ -419,6 +428,52 @@ def time_spec(T, dp, states, dev, stream, ev):
         "commit_state_gbps": round(2 * B * H * per_head / (com * 1e-3) / 1e9,
                                    1),
         "speedup_vs_decode_steps": round(dec / (ver + com), 3),
+    }
+
+
+def time_epilogue(po, dq, dk, dv, dg, dbeta, states, dev, stream, ev):
+    """Output epilogue: standalone over the prefill output (HBM GB/s), and
+    the decode step with the epilogue fused against the plain decode step."""
+    import torch
+    from linear_recurrent_attention_kda_amd import kda
+    gen = torch.Generator(device=dev).manual_seed(3)
+    z = torch.randn(po.shape, generator=gen, device=dev).to(po.dtype)
+    w = torch.randn(po.shape[-1], generator=gen, device=dev)
+    y = torch.empty_like(po)
+    zd = torch.randn(dq.shape[:2] + (dv.shape[-1],), generator=gen,
+                     device=dev).to(dq.dtype)
+    n = 10
+    for _ in range(3):
+        kda.kda_output_norm_gate(po, z, w, y=y)
+    a0, a1 = ev(), ev()
+    a0.record(stream)
+    for _ in range(n):
+        kda.kda_output_norm_gate(po, z, w, y=y)
+    a1.record(stream)
+    rec = []
+    for i in range(n + 3):
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record(stream)
+        kda.kda_decode_step_gated(dq, dk, dv, dg, dbeta, states[i % 3], zd, w)
+        e1.record(stream)
+        kda.kda_decode_step(dq, dk, dv, dg, dbeta, states[(i + 1) % 3])
+        e2.record(stream)
+        rec.append((e0, e1, e2))
+    torch.cuda.synchronize()
+    epi_ms = a0.elapsed_time(a1) / n
+    nbytes = 3 * po.numel() * po.element_size()
+    rec = rec[3:]
+    gated = float(np.mean([a.elapsed_time(b) for a, b, _ in rec]))
+    plain = float(np.mean([b.elapsed_time(c) for _, b, c in rec]))
+    log("epilogue: standalone %.4f ms; decode gated %.4f ms vs plain %.4f ms"
+        % (epi_ms, gated, plain))
+    return {
+        "standalone_rows": int(po.numel() // po.shape[-1]),
+        "standalone_ms": round(epi_ms, 5),
+        "standalone_gbps": round(nbytes / (epi_ms * 1e-3) / 1e9, 1),
+        "standalone_bytes": nbytes,
+        "decode_gated_ms": round(gated, 5),
+        "decode_plain_ms": round(plain, 5),
     }
 
 

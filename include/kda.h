@@ -189,6 +189,40 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v,
                              void* stream);
 
 /*
+ * Output epilogue of the KDA block ("Kimi K3: The Manos, The Mythos, The
+ * Legendos", section "Kimi Linear": the operator's output is normalised per
+ * head and scaled by an output gate, then a linear layer mixes the heads).
+ * Per (token, head) row of Dv channels:
+ *   y = o * rsqrt(mean(o^2) + eps) * w * sigmoid(z)
+ * with z the gate's pre-activation (the caller's linear transform of the
+ * block input) and w a per-channel weight shared by the heads.  One pass,
+ * bound by HBM bandwidth.
+ *   o, z, y [tokens, H, Dv] dtype (y may be o itself); w [Dv] fp32;
+ *   eps >= 0.
+ * tokens >= 0 (0 enqueues nothing); H >= 1; Dv in {16, 32, 64, 128}.
+ */
+kda_status_t kda_output_norm_gate(const void* o, const void* z,
+                                  const float* w, float eps, void* y,
+                                  int64_t tokens, int32_t H, int32_t Dv,
+                                  int32_t dtype, void* stream);
+
+/*
+ * kda_decode_step with the output epilogue fused: the step's output o never
+ * reaches memory; y = o * rsqrt(mean(o^2) + eps) * w * sigmoid(z) is
+ * written instead (see kda_output_norm_gate).  The state is updated exactly
+ * as by kda_decode_step.
+ *   z [B, H, Dv] dtype; w [Dv] fp32; y [B, H, Dv] dtype; eps >= 0.
+ * Other arguments as kda_decode_step.
+ */
+kda_status_t kda_decode_step_gated(const void* q, const void* k,
+                                   const void* v, const float* g,
+                                   const float* beta, float* state,
+                                   const void* z, const float* w, float eps,
+                                   void* y, int32_t B, int32_t H, int32_t Dk,
+                                   int32_t Dv, float scale, int32_t dtype,
+                                   void* stream);
+
+/*
  * Speculative-decode verify ("Model evolution after DeepSeek V3",
  * uncledou.site, section four: a cheap draft proposes several tokens and the
  * large model checks them in one parallel pass).  Runs T draft tokens of each

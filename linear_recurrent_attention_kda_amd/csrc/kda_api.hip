@@ -121,6 +121,36 @@ kda_status_t prefill_varlen(const void* q, const void* k, const void* v,
   return run_prefill(a, Dk, C, dtype, workspace, workspace_bytes, stream);
 }
 
+kda_status_t decode_step(const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, float* state,
+                         void* o, const void* z, const float* w, float eps,
+                         int32_t B, int32_t H, int32_t Dk, int32_t Dv,
+                         float scale, int32_t dtype, void* stream) {
+  if (B <= 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERR_INVALID_ARG;
+  if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_FP32)
+    return KDA_ERR_UNSUPPORTED;
+  if (!supported_dims(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > INT_MAX) return KDA_ERR_UNSUPPORTED;
+  kda_status_t st = check_tensors((int64_t)B, q, k, v, g, beta, o);
+  if (st != KDA_OK) return st;
+  if (!state || !aligned(state, 16)) return KDA_ERR_INVALID_ARG;
+
+  kda::DecodeArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.state = state;
+  a.o = o;
+  a.B = B;
+  a.H = H;
+  a.scale = scale;
+  a.z = z;
+  a.w = w;
+  a.eps = eps;
+  if (kda::launch_decode(a, Dk, dtype == KDA_DTYPE_BF16,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KDA_ERR_LAUNCH;
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -217,24 +247,46 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v,
                              void* o, int32_t B, int32_t H, int32_t Dk,
                              int32_t Dv, float scale, int32_t dtype,
                              void* stream) {
-  if (B <= 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERR_INVALID_ARG;
+  return decode_step(q, k, v, g, beta, state, o, nullptr, nullptr, 0.f, B, H,
+                     Dk, Dv, scale, dtype, stream);
+}
+
+kda_status_t kda_decode_step_gated(const void* q, const void* k,
+                                   const void* v, const float* g,
+                                   const float* beta, float* state,
+                                   const void* z, const float* w, float eps,
+                                   void* y, int32_t B, int32_t H, int32_t Dk,
+                                   int32_t Dv, float scale, int32_t dtype,
+                                   void* stream) {
+  if (!z || !w || !aligned(z, 16) || !aligned(w, 16) || !(eps >= 0.f))
+    return KDA_ERR_INVALID_ARG;
+  return decode_step(q, k, v, g, beta, state, y, z, w, eps, B, H, Dk, Dv,
+                     scale, dtype, stream);
+}
+
+kda_status_t kda_output_norm_gate(const void* o, const void* z,
+                                  const float* w, float eps, void* y,
+                                  int64_t tokens, int32_t H, int32_t Dv,
+                                  int32_t dtype, void* stream) {
+  if (tokens < 0 || H <= 0 || Dv <= 0 || !(eps >= 0.f))
+    return KDA_ERR_INVALID_ARG;
   if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_FP32)
     return KDA_ERR_UNSUPPORTED;
-  if (!supported_dims(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
-  if ((int64_t)B * H > INT_MAX) return KDA_ERR_UNSUPPORTED;
-  kda_status_t st = check_tensors((int64_t)B, q, k, v, g, beta, o);
-  if (st != KDA_OK) return st;
-  if (!state || !aligned(state, 16)) return KDA_ERR_INVALID_ARG;
-
-  kda::DecodeArgs a{};
-  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
-  a.state = state;
-  a.o = o;
-  a.B = B;
-  a.H = H;
-  a.scale = scale;
-  if (kda::launch_decode(a, Dk, dtype == KDA_DTYPE_BF16,
-                         static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (!supported_dims(Dv, Dv)) return KDA_ERR_UNSUPPORTED;
+  if (tokens == 0) return KDA_OK;
+  if (!o || !z || !w || !y) return KDA_ERR_INVALID_ARG;
+  if (!aligned(o, 16) || !aligned(z, 16) || !aligned(w, 16) ||
+      !aligned(y, 16))
+    return KDA_ERR_INVALID_ARG;
+  const int64_t rows = tokens * H;
+  // the grid covers rows in groups of 256 / (Dv / 4)
+  if (rows / (1024 / Dv) >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
+  kda::EpilogueArgs a{};
+  a.o = o; a.z = z; a.w = w; a.y = y;
+  a.rows = rows;
+  a.eps = eps;
+  if (kda::launch_epilogue(a, Dv, dtype == KDA_DTYPE_BF16,
+                           static_cast<hipStream_t>(stream)) != hipSuccess)
     return KDA_ERR_LAUNCH;
   return KDA_OK;
 }

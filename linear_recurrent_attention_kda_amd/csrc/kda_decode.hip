@@ -27,7 +27,7 @@
 namespace kda {
 namespace {
 
-template <typename Tio, int D, int NT, bool kNt>
+template <typename Tio, int D, int NT, bool kNt, bool kGated>
 __global__ __launch_bounds__(NT, (NT >= 1024 && sizeof(Tio) == 2) ? 8 : 1)
 void decode_kernel(DecodeArgs a) {
   constexpr int CG = D / 4;       // float4 column groups
@@ -114,14 +114,6 @@ void decode_kernel(DecodeArgs a) {
   u.z = beta * (io<Tio>::to_f(v[2]) - X.z);
   u.w = beta * (io<Tio>::to_f(v[3]) - X.w);
 
-  if (rg == 0) {
-    Tio* o = static_cast<Tio*>(a.o) + (size_t)bh * D + 4 * cg;
-    o[0] = io<Tio>::from_f(a.scale * (Y.x + QK * u.x));
-    o[1] = io<Tio>::from_f(a.scale * (Y.y + QK * u.y));
-    o[2] = io<Tio>::from_f(a.scale * (Y.z + QK * u.z));
-    o[3] = io<Tio>::from_f(a.scale * (Y.w + QK * u.w));
-  }
-
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int c = rg + RG * i;
@@ -132,6 +124,32 @@ void decode_kernel(DecodeArgs a) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), rs,
                                            (c * D + 4 * cg) * 4, 0, kPol);
   }
+
+  // output (after the state stores, so that the state's registers are free)
+  if (rg == 0) {
+    Tio* o = static_cast<Tio*>(a.o) + (size_t)bh * D + 4 * cg;
+    float ov[4] = {a.scale * (Y.x + QK * u.x), a.scale * (Y.y + QK * u.y),
+                   a.scale * (Y.z + QK * u.z), a.scale * (Y.w + QK * u.w)};
+    if (kGated) {
+      // output epilogue ("Kimi K3: The Manos, The Mythos, The Legendos",
+      // section "Kimi Linear": per-head norm, then the output gate); the
+      // CG lanes of this row are lanes 0 .. CG-1 of wave 0
+      float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
+#pragma unroll
+      for (int m = CG / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+      const float r = rsqrtf(ss * (1.f / D) + a.eps);
+      const Tio* z = static_cast<const Tio*>(a.z) + (size_t)bh * D + 4 * cg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float gate = 1.f / (1.f + __builtin_amdgcn_exp2f(
+                                            -io<Tio>::to_f(z[i]) * kLog2e));
+        ov[i] = ov[i] * r * a.w[4 * cg + i] * gate;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = io<Tio>::from_f(ov[i]);
+  }
+
 }
 
 // Launch shape: threads per workgroup (capped by D^2 / 4, one float4 per
@@ -162,10 +180,13 @@ template <typename Tio, int D, int NT>
 hipError_t launch_nt(const DecodeArgs& a, bool nt, hipStream_t st) {
   constexpr int T = (D * D / 4) < NT ? (D * D / 4) : NT;
   const unsigned blocks = (unsigned)a.B * (unsigned)a.H;
-  return nt ? launch_kernel(decode_kernel<Tio, D, T, true>, dim3(blocks),
-                            dim3(T), st, a)
-            : launch_kernel(decode_kernel<Tio, D, T, false>, dim3(blocks),
-                            dim3(T), st, a);
+  if (a.z)  // fused output epilogue: default cache policy shape only
+    return launch_kernel(decode_kernel<Tio, D, T, true, true>, dim3(blocks),
+                         dim3(T), st, a);
+  return nt ? launch_kernel(decode_kernel<Tio, D, T, true, false>,
+                            dim3(blocks), dim3(T), st, a)
+            : launch_kernel(decode_kernel<Tio, D, T, false, false>,
+                            dim3(blocks), dim3(T), st, a);
 }
 
 template <typename Tio, int D>

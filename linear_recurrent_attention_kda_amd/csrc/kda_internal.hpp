@@ -100,6 +100,15 @@ struct DecodeArgs {
   float* state; void* o;
   int32_t B, H;
   float scale;
+  // output epilogue fused into the decode step (when z != nullptr): o is
+  // replaced by o * rsqrt(mean(o^2) + eps) * w * sigmoid(z)
+  const void* z; const float* w; float eps;
+};
+
+struct EpilogueArgs {
+  const void* o; const void* z; const float* w; void* y;
+  int64_t rows;                // tokens * heads
+  float eps;
 };
 
 // Launch a kernel whose only parameter is `arg`; returns the launch status
@@ -122,5 +131,7 @@ hipError_t launch_recur(const PrefillArgs& a, int D, int C, bool bf16_io,
 hipError_t launch_spec(const SpecArgs& a, int D, bool bf16_io, bool commit,
                        hipStream_t s);
 int max_spec_tokens();
+hipError_t launch_epilogue(const EpilogueArgs& a, int D, bool bf16_io,
+                           hipStream_t s);
 
 }  // namespace kda

@@ -74,6 +74,13 @@ def load() -> ctypes.CDLL:
         lib.kda_spec_commit.restype = i32
         lib.kda_spec_commit.argtypes = [
             vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+        lib.kda_output_norm_gate.restype = i32
+        lib.kda_output_norm_gate.argtypes = [vp, vp, vp, f32, vp, i64, i32,
+                                             i32, i32, vp]
+        lib.kda_decode_step_gated.restype = i32
+        lib.kda_decode_step_gated.argtypes = [
+            vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32, i32, f32,
+            i32, vp]
         lib.kda_decode_step.restype = i32
         lib.kda_decode_step.argtypes = [
             vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
@@ -376,3 +383,58 @@ def kda_spec_commit(k, g, u, accepted, state):
     if st != KDA_OK:
         raise KDAError("kda_spec_commit", st)
     return state
+
+
+def kda_output_norm_gate(o, z, w, *, eps: float = 1e-6, y=None):
+    """y = o * rsqrt(mean(o^2) + eps) * w * sigmoid(z) per (token, head) row.
+
+    o, z: [..., H, Dv] (bf16 or fp32, same dtype); w: [Dv] fp32.  y may be
+    o itself.  Returns y.
+    """
+    lib = load()
+    Dv = o.shape[-1]
+    H = o.shape[-2]
+    tokens = o.numel() // (H * Dv) if o.numel() else 0
+    dev = o.device
+    _check(z, "z", tuple(o.shape), o.dtype, dev)
+    _check(w, "w", (Dv,), torch.float32, dev)
+    if not o.is_contiguous():
+        raise ValueError("o must be contiguous")
+    if y is None:
+        y = torch.empty_like(o)
+    _check(y, "y", tuple(o.shape), o.dtype, dev)
+    st = lib.kda_output_norm_gate(_ptr(o), _ptr(z), _ptr(w), eps, _ptr(y),
+                                  tokens, H, Dv, _dtype_code(o), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_output_norm_gate", st)
+    return y
+
+
+def kda_decode_step_gated(q, k, v, g, beta, state, z, w, *,
+                          eps: float = 1e-6, scale: float = 1.0, y=None):
+    """kda_decode_step with the output epilogue fused: returns
+    y = o * rsqrt(mean(o^2) + eps) * w * sigmoid(z) [B, H, Dv]; `state` is
+    updated in place."""
+    lib = load()
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    for t, n, s_, dt in ((q, "q", (B, H, Dk), q.dtype),
+                         (k, "k", (B, H, Dk), q.dtype),
+                         (v, "v", (B, H, Dv), q.dtype),
+                         (g, "g", (B, H, Dk), torch.float32),
+                         (beta, "beta", (B, H), torch.float32),
+                         (state, "state", (B, H, Dk, Dv), torch.float32),
+                         (z, "z", (B, H, Dv), q.dtype),
+                         (w, "w", (Dv,), torch.float32)):
+        _check(t, n, s_, dt, dev)
+    if y is None:
+        y = torch.empty((B, H, Dv), dtype=q.dtype, device=dev)
+    _check(y, "y", (B, H, Dv), q.dtype, dev)
+    st = lib.kda_decode_step_gated(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(z),
+        _ptr(w), eps, _ptr(y), B, H, Dk, Dv, scale, _dtype_code(q),
+        _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_decode_step_gated", st)
+    return y

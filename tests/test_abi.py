@@ -25,7 +25,8 @@ def test_exports_every_declared_symbol():
                           "kda_prefill_workspace_size", "kda_prefill_chunked",
                           "kda_prefill_varlen", "kda_prefill_varlen_ckpt",
                           "kda_decode_step", "kda_spec_verify",
-                          "kda_spec_commit"}
+                          "kda_spec_commit", "kda_output_norm_gate",
+                          "kda_decode_step_gated"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -192,3 +193,35 @@ def test_spec_validation():
     assert _commit(lib, state=NULL) == INVALID
     assert _commit(lib, u=MIS) == INVALID
     assert _commit(lib, Dk=64, Dv=128) == UNSUP
+
+
+def _epi(lib, **kw):
+    a = dict(o=P, z=P, w=P, eps=1e-6, y=P, tokens=10, H=2, Dv=128, dtype=0,
+             stream=NULL)
+    a.update(kw)
+    return lib.kda_output_norm_gate(a["o"], a["z"], a["w"], a["eps"], a["y"],
+                                    a["tokens"], a["H"], a["Dv"], a["dtype"],
+                                    a["stream"])
+
+
+def test_epilogue_validation():
+    """Every call here fails validation or has nothing to do."""
+    lib = kda.load()
+    assert _epi(lib, tokens=-1) == INVALID
+    assert _epi(lib, H=0) == INVALID
+    assert _epi(lib, eps=-1.0) == INVALID
+    assert _epi(lib, eps=float("nan")) == INVALID
+    assert _epi(lib, Dv=96) == UNSUP
+    assert _epi(lib, dtype=9) == UNSUP
+    assert _epi(lib, z=NULL) == INVALID
+    assert _epi(lib, w=MIS) == INVALID
+    assert _epi(lib, tokens=0) == OK            # nothing enqueued
+    gated = lambda **kw: lib.kda_decode_step_gated(  # noqa: E731
+        kw.get("q", P), P, P, P, P, kw.get("state", P), kw.get("z", P),
+        kw.get("w", P), kw.get("eps", 1e-6), P, kw.get("B", 2), 2, 128, 128,
+        1.0, 0, NULL)
+    assert gated(z=NULL) == INVALID
+    assert gated(w=NULL) == INVALID
+    assert gated(eps=-0.5) == INVALID
+    assert gated(B=0) == INVALID
+    assert gated(state=MIS) == INVALID
