@@ -106,6 +106,9 @@ def main(argv=None):
                     help="also time the output epilogue: standalone over the "
                          "prefill output, and fused into the decode step "
                          "(outside the timed steps)")
+    ap.add_argument("--prologue", action="store_true",
+                    help="also time the prefill with the input prologue "
+                         "fused (outside the timed steps)")
     ap.add_argument("--step-only", action="store_true",
                     help="skip the measurements taken after the timed steps "
                          "(back-to-back decode, reference copy), so that a "
@@ -273,6 +276,9 @@ def main(argv=None):
     spec = None
     if args.spec_tokens and not args.step_only:
         spec = time_spec(args.spec_tokens, dp, states, dev, stream, ev)
+    pro = None
+    if args.prologue and not args.step_only:
+        pro = time_prologue(pp, nseq, total, ws, dev, stream, ev)
     epi = None
     if args.epilogue and not args.step_only:
         epi = time_epilogue(po, dq, dk, dv, dg, dbeta, states, dev, stream, ev)
@@ -370,6 +376,9 @@ def main(argv=None):
         result["spec"] = spec
     if epi is not None:
         result["epilogue"] = epi
+    if pro is not None:
+        pro["plain_prefill_ms"] = round(pre_avg, 5)
+        result["prologue"] = pro
 
     # ---------------- CPU baseline: the oracle on the host cores -----------
     if not args.no_cpu_baseline:
@@ -429,6 +438,46 @@ def time_spec(T, dp, states, dev, stream, ev):
                                    1),
         "speedup_vs_decode_steps": round(dec / (ver + com), 3),
     }
+
+
+def time_prologue(pp, nseq, total, ws, dev, stream, ev):
+    """Prefill of the same shape with the input prologue fused into the
+    chunk-prep kernel (random projected inputs, taps and gate
+    pre-activations)."""
+    import torch
+    from linear_recurrent_attention_kda_amd import kda
+    gen = torch.Generator(device=dev).manual_seed(4)
+    rn = lambda *shape: torch.randn(shape, generator=gen,  # noqa: E731
+                                    device=dev)
+    xq, xk = (rn(total, pp.H, pp.K).to(torch.bfloat16) for _ in range(2))
+    xv = rn(total, pp.H, pp.V).to(torch.bfloat16)
+    w = rn(3, pp.H, pp.K, 4) * 0.5
+    a, b = rn(total, pp.H, pp.K), rn(total, pp.H)
+    if pp.kind == "varlen":
+        cu = torch.from_numpy(pp.cu_seqlens).to(dev)
+        maxlen = int(pp.seq_lengths.max())
+    else:
+        cu = torch.arange(nseq + 1, dtype=torch.int32, device=dev) * pp.T
+        maxlen = pp.T
+    o = torch.empty((total, pp.H, pp.V), dtype=torch.bfloat16, device=dev)
+    fs = torch.empty((nseq, pp.H, pp.K, pp.V), dtype=torch.float32,
+                     device=dev)
+    run = lambda: kda.kda_prefill_varlen_prologue(  # noqa: E731
+        xq, xk, xv, w, a, b, cu, maxlen, None, chunk_size=pp.C,
+        final_state=fs, o=o, workspace=ws)
+    for _ in range(3):
+        run()
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    n = 10
+    for _ in range(n):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    log("prologue-fused prefill: %.4f ms" % ms)
+    return {"fused_prefill_ms": round(ms, 5),
+            "tokens_per_s": round(total / (ms * 1e-3), 1)}
 
 
 def time_epilogue(po, dq, dk, dv, dg, dbeta, states, dev, stream, ev):

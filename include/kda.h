@@ -173,6 +173,33 @@ kda_status_t kda_prefill_varlen_ckpt(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_prefill_varlen with the block's input prologue fused into the
+ * chunk-prep kernel ("Kimi K3: The Manos, The Mythos, The Legendos", section
+ * "Kimi Linear": after their projections, query, key and value pass through
+ * a short convolution, left-padded to stay causal, and query and key are
+ * L2-normalised; the decay gate and beta come from projections).  Per
+ * (token, head), with sequences restarting at cu_seqlens boundaries:
+ *   conv(x)[t, c] = sum_{j=0..3} conv_w[., h, c, j] * x[t - 3 + j, c]
+ *                   (x = 0 before the sequence's first token)
+ *   q = conv(xq) / ||conv(xq)||   k = conv(xk) / ||conv(xk)||   v = conv(xv)
+ *   g = -5 * sigmoid(a)   (so the g_min = -5 bound holds by construction)
+ *   beta = sigmoid(b)
+ * and then exactly kda_prefill_varlen on (q, k, v, g, beta); q, k, v are
+ * rounded to the storage dtype before use, as stored inputs would be.
+ *   xq, xk [total_T, H, Dk], xv [total_T, H, Dv]   dtype
+ *   conv_w [3, H, D, 4] fp32 (taps for q, k, v; tap 3 is the current token)
+ *   a      [total_T, H, Dk] fp32;   b [total_T, H] fp32
+ * All other arguments, and every error, as kda_prefill_varlen.
+ */
+kda_status_t kda_prefill_varlen_prologue(
+    const void* xq, const void* xk, const void* xv, const float* conv_w,
+    const float* a, const float* b, const int32_t* cu_seqlens, int32_t N,
+    int64_t total_T, int32_t max_seqlen, const float* initial_state,
+    float* final_state, void* o, int32_t H, int32_t Dk, int32_t Dv, int32_t C,
+    float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/*
  * One decode token for each of B sequences ("FlashKDA algorithm": decode
  * follows the per-token form; "Complexity analysis": the fp32 state read and
  * write dominate, about 8*Dk*Dv bytes per head).  The state is read once and

@@ -77,8 +77,8 @@ kda_status_t prefill_varlen(const void* q, const void* k, const void* v,
                             int32_t C, float scale, int32_t dtype,
                             bool want_ckpt, int32_t ckpt_every,
                             float* ckpt_states, size_t ckpt_bytes,
-                            void* workspace, size_t workspace_bytes,
-                            void* stream) {
+                            const float* conv_w, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   if (N <= 0 || total_T < 0 || max_seqlen < 0) return KDA_ERR_INVALID_ARG;
   if (total_T > 0 && max_seqlen == 0) return KDA_ERR_INVALID_ARG;
   kda_status_t st = check_prefill_common(H, Dk, Dv, C, dtype);
@@ -118,6 +118,7 @@ kda_status_t prefill_varlen(const void* q, const void* k, const void* v,
   a.ckpt_every = want_ckpt ? ckpt_every : 0;
   a.ckpt_states =
       (want_ckpt && total_T / ckpt_every > 0) ? ckpt_states : nullptr;
+  a.conv_w = conv_w;
   return run_prefill(a, Dk, C, dtype, workspace, workspace_bytes, stream);
 }
 
@@ -225,7 +226,7 @@ kda_status_t kda_prefill_varlen(const void* q, const void* k, const void* v,
                                 size_t workspace_bytes, void* stream) {
   return prefill_varlen(q, k, v, g, beta, cu_seqlens, N, total_T, max_seqlen,
                         initial_state, final_state, o, H, Dk, Dv, C, scale,
-                        dtype, false, 0, nullptr, 0, workspace,
+                        dtype, false, 0, nullptr, 0, nullptr, workspace,
                         workspace_bytes, stream);
 }
 
@@ -239,7 +240,21 @@ kda_status_t kda_prefill_varlen_ckpt(
   return prefill_varlen(q, k, v, g, beta, cu_seqlens, N, total_T, max_seqlen,
                         initial_state, final_state, o, H, Dk, Dv, C, scale,
                         dtype, true, ckpt_every, ckpt_states, ckpt_bytes,
-                        workspace, workspace_bytes, stream);
+                        nullptr, workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_prefill_varlen_prologue(
+    const void* xq, const void* xk, const void* xv, const float* conv_w,
+    const float* a, const float* b, const int32_t* cu_seqlens, int32_t N,
+    int64_t total_T, int32_t max_seqlen, const float* initial_state,
+    float* final_state, void* o, int32_t H, int32_t Dk, int32_t Dv, int32_t C,
+    float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (!conv_w || !aligned(conv_w, 16)) return KDA_ERR_INVALID_ARG;
+  return prefill_varlen(xq, xk, xv, a, b, cu_seqlens, N, total_T, max_seqlen,
+                        initial_state, final_state, o, H, Dk, Dv, C, scale,
+                        dtype, false, 0, nullptr, 0, conv_w, workspace,
+                        workspace_bytes, stream);
 }
 
 kda_status_t kda_decode_step(const void* q, const void* k, const void* v,

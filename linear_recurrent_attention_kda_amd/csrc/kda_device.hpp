@@ -62,6 +62,10 @@ template <> struct Raw8<bf16> {
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
   }
+  __device__ __forceinline__ void set(const float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (bf16)x[i];
+  }
 };
 template <> struct Raw8<float> {
   float4 lo, hi;
@@ -82,6 +86,10 @@ template <> struct Raw8<float> {
   __device__ __forceinline__ void get(float (&x)[8]) const {
     x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w;
     x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
+  }
+  __device__ __forceinline__ void set(const float (&x)[8]) {
+    lo = make_float4(x[0], x[1], x[2], x[3]);
+    hi = make_float4(x[4], x[5], x[6], x[7]);
   }
 };
 

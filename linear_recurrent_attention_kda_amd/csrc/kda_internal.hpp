@@ -81,6 +81,11 @@ struct PrefillArgs {
   int64_t nslots;
   float* ckpt_states;          // state checkpoints, or nullptr
   int32_t ckpt_every;          // checkpoint interval in tokens (multiple of C)
+  // Input prologue fused into the chunk-prep kernel when conv_w != nullptr:
+  // q, k, v then hold the short convolutions' inputs, g the decay gate's
+  // pre-activation a (g = -5 sigmoid(a)) and beta the pre-activation b
+  // (beta = sigmoid(b)); conv_w is [3, H, D, 4] fp32 (taps of q, k, v).
+  const float* conv_w;
 };
 
 struct SpecArgs {

@@ -52,7 +52,7 @@ namespace {
 // workgroups running together read whole contiguous token rows.
 struct Item {
   int n, ci, h;
-  int64_t t0;
+  int64_t bos, t0;
   int L;
   bool valid;
 };
@@ -67,6 +67,7 @@ __device__ __forceinline__ Item decode_item(const PrefillArgs& a, int C,
   it.n = (int)(rest / (uint32_t)a.max_chunks);
   int64_t bos, eos;
   seq_bounds(a, it.n, bos, eos);
+  it.bos = bos;
   it.t0 = bos + (int64_t)it.ci * C;
   it.valid = it.t0 < eos;
   it.L = it.valid ? ((eos - it.t0) < C ? (int)(eos - it.t0) : C) : 0;
@@ -93,7 +94,11 @@ __device__ __forceinline__ void store_bf16xn(bf16* p, const float (&x)[N]) {
   }
 }
 
-template <typename Tin, int D, int C>
+// Taps of the input prologue's short convolution (the current token and the
+// three before it).
+constexpr int kConvTaps = 4;
+
+template <typename Tin, int D, int C, bool kPro>
 __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
   constexpr int NT = 256, NW = NT / kWave;  // threads, waves
   constexpr int K = D, V = D;
@@ -135,6 +140,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) float s_rho[NSUB + 1][D];
   __shared__ float s_beta[C];
   float (*s_wtot)[D] = reinterpret_cast<float (*)[D]>(s_r);
+  // prologue taps [3][D][4], staged before the scan, read only by stage 0
+  constexpr int R_TAPS = NW * D * 4;
+  static_assert(!kPro || R_TAPS + 3 * D * kConvTaps * 4 <= R_BYTES,
+                "prologue taps fit in the shared region");
+  float (*s_taps)[D][kConvTaps] =
+      reinterpret_cast<float (*)[D][kConvTaps]>(s_r + R_TAPS);
   bf16 (*s_qh)[RP] = reinterpret_cast<bf16 (*)[RP]>(s_r);
   bf16 (*s_kh)[RP] = reinterpret_cast<bf16 (*)[RP]>(s_r + C * RP * 2);
   bf16 (*s_kcb)[RP] = reinterpret_cast<bf16 (*)[RP]>(s_r + 2 * C * RP * 2);
@@ -188,31 +199,142 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
 
   float gx[RPT][8], bt[RPT];
   Raw8<Tin> rq[RPT], rk[RPT], rv[RPT];
-  if (active) {
+  if (!kPro) {
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const uint32_t row = (uint32_t)((r0 + i) * H);
+        const uint4 g0 = buffer_load_16(Rg, (row * K + c0) * 4);
+        const uint4 g1 = buffer_load_16(Rg, (row * K + c0 + 4) * 4);
+        gx[i][0] = __uint_as_float(g0.x); gx[i][1] = __uint_as_float(g0.y);
+        gx[i][2] = __uint_as_float(g0.z); gx[i][3] = __uint_as_float(g0.w);
+        gx[i][4] = __uint_as_float(g1.x); gx[i][5] = __uint_as_float(g1.y);
+        gx[i][6] = __uint_as_float(g1.z); gx[i][7] = __uint_as_float(g1.w);
+        rq[i].load_buf(Rq, (row * K + c0) * sizeof(Tin));
+        rk[i].load_buf(Rk, (row * K + c0) * sizeof(Tin));
+        rv[i].load_buf(Rv, (row * V + c0) * sizeof(Tin));
+        bt[i] = buffer_load_f32(Rb, row * 4);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gx[i][e] = 0.f;
+        rq[i].zero();
+        rk[i].zero();
+        rv[i].zero();
+        bt[i] = 0.f;
+      }
+    }
+  } else {
+    // ---- 0'. input prologue ("Kimi K3: The Manos, The Mythos, The
+    //          Legendos", section "Kimi Linear"): causal short convolutions
+    //          of q, k, v (zero left padding at the sequence start), L2 norm
+    //          of q and k per head, g = -5 sigmoid(a), beta = sigmoid(b).
+    //          The convolution window of row r is rows r-3 .. r; this
+    //          thread's window rows are r0-3 .. r0+RPT-1, addressed from the
+    //          later of the sequence start and t0 - 3, so that rows before
+    //          the sequence start wrap to an out-of-range offset and load 0.
+    constexpr int NWIN = RPT + kConvTaps - 1;
+    const int64_t wb = it.t0 - (kConvTaps - 1) > it.bos
+                           ? it.t0 - (kConvTaps - 1) : it.bos;
+    const int64_t wrow0 = wb * H + h;
+    const int64_t wspan = (it.t0 + it.L - 1 - wb) * H;
+    const __amdgpu_buffer_rsrc_t Wq = make_rsrc(
+        static_cast<const Tin*>(a.q) + wrow0 * K,
+        (uint32_t)((wspan * K + K) * sizeof(Tin)));
+    const __amdgpu_buffer_rsrc_t Wk = make_rsrc(
+        static_cast<const Tin*>(a.k) + wrow0 * K,
+        (uint32_t)((wspan * K + K) * sizeof(Tin)));
+    const __amdgpu_buffer_rsrc_t Wv = make_rsrc(
+        static_cast<const Tin*>(a.v) + wrow0 * V,
+        (uint32_t)((wspan * V + V) * sizeof(Tin)));
+    // taps of this head: [3][D][4] fp32, staged in LDS
+    const float* taps = a.conv_w + (size_t)h * D * kConvTaps;
+    for (int e = tid; e < 3 * D * kConvTaps; e += NT) {
+      const int x = e / (D * kConvTaps), rem = e % (D * kConvTaps);
+      s_taps[x][rem / kConvTaps][rem % kConvTaps] =
+          taps[(size_t)x * H * D * kConvTaps + rem];
+    }
+    Raw8<Tin> wq[NWIN], wk[NWIN], wv[NWIN];
+    // window row j of this thread is packed row t0 + r0 - 3 + j; its offset
+    // from wb is negative (huge as unsigned: loads 0) before the sequence
+    const int64_t d0 = it.t0 + r0 - (kConvTaps - 1) - wb;
+#pragma unroll
+    for (int j = 0; j < NWIN; ++j) {
+      const uint32_t row = (uint32_t)((d0 + j) * H);
+      if (active) {
+        wq[j].load_buf(Wq, (row * K + c0) * sizeof(Tin));
+        wk[j].load_buf(Wk, (row * K + c0) * sizeof(Tin));
+        wv[j].load_buf(Wv, (row * V + c0) * sizeof(Tin));
+      } else {
+        wq[j].zero();
+        wk[j].zero();
+        wv[j].zero();
+      }
+    }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const uint32_t row = (uint32_t)((r0 + i) * H);
-      const uint4 g0 = buffer_load_16(Rg, (row * K + c0) * 4);
-      const uint4 g1 = buffer_load_16(Rg, (row * K + c0 + 4) * 4);
-      gx[i][0] = __uint_as_float(g0.x); gx[i][1] = __uint_as_float(g0.y);
-      gx[i][2] = __uint_as_float(g0.z); gx[i][3] = __uint_as_float(g0.w);
-      gx[i][4] = __uint_as_float(g1.x); gx[i][5] = __uint_as_float(g1.y);
-      gx[i][6] = __uint_as_float(g1.z); gx[i][7] = __uint_as_float(g1.w);
-      rq[i].load_buf(Rq, (row * K + c0) * sizeof(Tin));
-      rk[i].load_buf(Rk, (row * K + c0) * sizeof(Tin));
-      rv[i].load_buf(Rv, (row * V + c0) * sizeof(Tin));
-      bt[i] = buffer_load_f32(Rb, row * 4);
-    }
-  } else {
+      float av[8];
+      if (active) {
+        const uint4 g0 = buffer_load_16(Rg, (row * K + c0) * 4);
+        const uint4 g1 = buffer_load_16(Rg, (row * K + c0 + 4) * 4);
+        av[0] = __uint_as_float(g0.x); av[1] = __uint_as_float(g0.y);
+        av[2] = __uint_as_float(g0.z); av[3] = __uint_as_float(g0.w);
+        av[4] = __uint_as_float(g1.x); av[5] = __uint_as_float(g1.y);
+        av[6] = __uint_as_float(g1.z); av[7] = __uint_as_float(g1.w);
+        bt[i] = buffer_load_f32(Rb, row * 4);
+      } else {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
+        for (int e = 0; e < 8; ++e) av[e] = 0.f;
+        bt[i] = 0.f;
+      }
+      // rows past L must keep g = 0 and beta = 0 (no decay, no write)
+      const bool live = r0 + i < it.L;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gx[i][e] = 0.f;
-      rq[i].zero();
-      rk[i].zero();
-      rv[i].zero();
-      bt[i] = 0.f;
+      for (int e = 0; e < 8; ++e)
+        gx[i][e] = live ? -5.f / (1.f + __builtin_amdgcn_exp2f(-av[e] * kLog2e))
+                        : 0.f;
+      bt[i] = live ? 1.f / (1.f + __builtin_amdgcn_exp2f(-bt[i] * kLog2e))
+                   : 0.f;
     }
+    __syncthreads();  // taps staged
+    auto conv_rows = [&](const Raw8<Tin> (&win)[NWIN], int x, bool normalise,
+                         Raw8<Tin> (&out)[RPT]) {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kConvTaps; ++j) {
+          float xv[8];
+          win[i + j].get(xv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += s_taps[x][c0 + e][j] * xv[e];
+        }
+        if (r0 + i >= it.L) {  // padding rows of a partial chunk stay 0
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        }
+        if (normalise) {
+          // the row's D channels are spread over CGN consecutive lanes
+          float ss = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss += acc[e] * acc[e];
+#pragma unroll
+          for (int m = CGN / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+          const float r = ss > 0.f ? rsqrtf(ss) : 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] *= r;
+        }
+        out[i].set(acc);
+      }
+    };
+    conv_rows(wq, 0, true, rq);
+    conv_rows(wk, 1, true, rk);
+    conv_rows(wv, 2, false, rv);
+    // the scan's barriers separate these reads of the taps from stage 2,
+    // which reuses their storage
   }
 
   // ---- 1. cumulative log2-decay a (registers): inclusive scan over the
@@ -505,7 +627,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
 template <typename Tin, int D, int C>
 hipError_t launch(const PrefillArgs& a, hipStream_t st) {
   const int64_t items = (int64_t)a.N * a.max_chunks * a.H;
-  return launch_kernel(prep_kernel<Tin, D, C>, dim3((unsigned)items),
+  if (a.conv_w)
+    return launch_kernel(prep_kernel<Tin, D, C, true>, dim3((unsigned)items),
+                         dim3(256), st, a);
+  return launch_kernel(prep_kernel<Tin, D, C, false>, dim3((unsigned)items),
                        dim3(256), st, a);
 }
 

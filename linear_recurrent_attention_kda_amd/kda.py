@@ -81,6 +81,10 @@ def load() -> ctypes.CDLL:
         lib.kda_decode_step_gated.argtypes = [
             vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32, i32, f32,
             i32, vp]
+        lib.kda_prefill_varlen_prologue.restype = i32
+        lib.kda_prefill_varlen_prologue.argtypes = [
+            vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, i32, i32,
+            i32, i32, f32, i32, vp, sz, vp]
         lib.kda_decode_step.restype = i32
         lib.kda_decode_step.argtypes = [
             vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
@@ -438,3 +442,48 @@ def kda_decode_step_gated(q, k, v, g, beta, state, z, w, *,
     if st != KDA_OK:
         raise KDAError("kda_decode_step_gated", st)
     return y
+
+
+def kda_prefill_varlen_prologue(xq, xk, xv, conv_w, a, b, cu_seqlens,
+                                max_seqlen: int, initial_state=None, *,
+                                chunk_size: int = 64, scale: float = 1.0,
+                                output_final_state: bool = True,
+                                final_state=None, o=None, workspace=None):
+    """kda_prefill_varlen with the input prologue fused: xq, xk, xv
+    [total_T, H, D] (inputs of the short convolutions), conv_w [3, H, D, 4]
+    fp32, a [total_T, H, Dk] fp32 (g = -5 sigmoid(a)), b [total_T, H] fp32
+    (beta = sigmoid(b)).  Returns (o, final_state)."""
+    lib = load()
+    total_T, H, Dk = xq.shape
+    Dv = xv.shape[-1]
+    dev = xq.device
+    N = cu_seqlens.numel() - 1
+    for t, n, s_, dt in ((xq, "xq", (total_T, H, Dk), xq.dtype),
+                         (xk, "xk", (total_T, H, Dk), xq.dtype),
+                         (xv, "xv", (total_T, H, Dv), xq.dtype),
+                         (conv_w, "conv_w", (3, H, Dk, 4), torch.float32),
+                         (a, "a", (total_T, H, Dk), torch.float32),
+                         (b, "b", (total_T, H), torch.float32),
+                         (cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)):
+        _check(t, n, s_, dt, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (N, H, Dk, Dv), torch.float32,
+               dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32,
+                                  device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (N, H, Dk, Dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((total_T, H, Dv), dtype=xq.dtype, device=dev)
+    _check(o, "o", (total_T, H, Dv), xq.dtype, dev)
+    if workspace is None:
+        workspace = workspace_for(N, total_T, H, Dk, Dv, chunk_size, dev)
+    st = lib.kda_prefill_varlen_prologue(
+        _ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_w), _ptr(a), _ptr(b),
+        _ptr(cu_seqlens), N, total_T, int(max_seqlen), _ptr(initial_state),
+        _ptr(final_state), _ptr(o), H, Dk, Dv, chunk_size, scale,
+        _dtype_code(xq), _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_prefill_varlen_prologue", st)
+    return o, final_state

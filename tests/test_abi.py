@@ -26,7 +26,8 @@ def test_exports_every_declared_symbol():
                           "kda_prefill_varlen", "kda_prefill_varlen_ckpt",
                           "kda_decode_step", "kda_spec_verify",
                           "kda_spec_commit", "kda_output_norm_gate",
-                          "kda_decode_step_gated"}
+                          "kda_decode_step_gated",
+                          "kda_prefill_varlen_prologue"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -225,3 +226,23 @@ def test_epilogue_validation():
     assert gated(eps=-0.5) == INVALID
     assert gated(B=0) == INVALID
     assert gated(state=MIS) == INVALID
+
+
+def test_prologue_validation():
+    """Every call here fails validation (nothing is launched)."""
+    lib = kda.load()
+
+    def call(**kw):
+        a = dict(xq=P, xk=P, xv=P, w=P, a=P, b=P, cu=P, N=2, total=100,
+                 maxlen=64, H=2, D=64, C=64, dtype=0, ws=P, ws_bytes=1 << 40)
+        a.update(kw)
+        return lib.kda_prefill_varlen_prologue(
+            a["xq"], a["xk"], a["xv"], a["w"], a["a"], a["b"], a["cu"],
+            a["N"], a["total"], a["maxlen"], NULL, NULL, P, a["H"], a["D"],
+            a["D"], a["C"], 1.0, a["dtype"], a["ws"], a["ws_bytes"], NULL)
+    assert call(w=NULL) == INVALID
+    assert call(w=ctypes.c_void_p(0x100004)) == INVALID
+    assert call(N=0) == INVALID
+    assert call(a=NULL) == INVALID
+    assert call(D=96) == UNSUP
+    assert call(ws_bytes=100) == WS
