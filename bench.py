@@ -538,7 +538,12 @@ def cpu_baseline(dp, pp):
     oracle.run_decode(dp.q, dp.k, dp.v, dp.g, dp.beta, dp.initial_state)
     dec_s = time.perf_counter() - t
     dec_bytes = counts.decode_bytes_per_head(dp.K) * dp.B * dp.H
-    heads = list(range(min(threads, pp.H)))
+    # prefill sample: about 96 x 8192 token-heads (the whole 8K-token,
+    # 96-head workload; a proportional number of heads of larger ones)
+    total_tokens = (int(pp.cu_seqlens[-1]) if pp.kind == "varlen"
+                    else pp.B * pp.T)
+    nh = max(1, min(pp.H, (96 * 8192) // max(1, total_tokens)))
+    heads = list(range(nh))
     sel = lambda x: x[..., heads, :]  # noqa: E731
     t = time.perf_counter()
     if pp.kind == "varlen":
