@@ -39,7 +39,14 @@ void decode_kernel(DecodeArgs a) {
   static_assert(32 % CG == 0 && NT >= 64, "decode lane grouping");
 
   __shared__ float s_alpha[D], s_k[D], s_q[D];
-  __shared__ float4 s_red[NW][CG][3];
+  // cross-wave partial sums: with many waves, one thread per (component,
+  // column group) sums the waves and every thread then reads 9 totals,
+  // instead of every thread reading every wave's partials (16x the LDS
+  // traffic at 16 waves)
+  constexpr bool kTwoLevel = NW >= 8;
+  __shared__ float4 s_red[kTwoLevel ? 1 : NW][CG][3];
+  __shared__ float s_part[kTwoLevel ? NW : 1][9][CG];
+  __shared__ float s_fin[kTwoLevel ? 9 : 1][CG];
 
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
@@ -87,23 +94,46 @@ void decode_kernel(DecodeArgs a) {
     }
     qk += __shfl_xor(qk, off);
   }
-  if ((tid & 63) < CG) {
-    const int w = tid / 64;
-    s_red[w][cg][0] = make_float4(x[0], x[1], x[2], x[3]);
-    s_red[w][cg][1] = make_float4(y[0], y[1], y[2], y[3]);
-    s_red[w][cg][2] = make_float4(qk, 0.f, 0.f, 0.f);
-  }
-  __syncthreads();
-
   float4 X = make_float4(0.f, 0.f, 0.f, 0.f);
   float4 Y = make_float4(0.f, 0.f, 0.f, 0.f);
   float QK = 0.f;
+  if constexpr (kTwoLevel) {
+    if ((tid & 63) < CG) {
+      const int w = tid / 64;
 #pragma unroll
-  for (int r = 0; r < NW; ++r) {
-    const float4 xr = s_red[r][cg][0], yr = s_red[r][cg][1];
-    X.x += xr.x; X.y += xr.y; X.z += xr.z; X.w += xr.w;
-    Y.x += yr.x; Y.y += yr.y; Y.z += yr.z; Y.w += yr.w;
-    QK += s_red[r][cg][2].x;
+      for (int j = 0; j < 4; ++j) {
+        s_part[w][j][cg] = x[j];
+        s_part[w][4 + j][cg] = y[j];
+      }
+      s_part[w][8][cg] = qk;
+    }
+    __syncthreads();
+    if (tid < 9 * CG) {
+      const int comp = tid / CG, c = tid % CG;
+      float t = 0.f;
+#pragma unroll
+      for (int r = 0; r < NW; ++r) t += s_part[r][comp][c];
+      s_fin[comp][c] = t;
+    }
+    __syncthreads();
+    X = make_float4(s_fin[0][cg], s_fin[1][cg], s_fin[2][cg], s_fin[3][cg]);
+    Y = make_float4(s_fin[4][cg], s_fin[5][cg], s_fin[6][cg], s_fin[7][cg]);
+    QK = s_fin[8][cg];
+  } else {
+    if ((tid & 63) < CG) {
+      const int w = tid / 64;
+      s_red[w][cg][0] = make_float4(x[0], x[1], x[2], x[3]);
+      s_red[w][cg][1] = make_float4(y[0], y[1], y[2], y[3]);
+      s_red[w][cg][2] = make_float4(qk, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < NW; ++r) {
+      const float4 xr = s_red[r][cg][0], yr = s_red[r][cg][1];
+      X.x += xr.x; X.y += xr.y; X.z += xr.z; X.w += xr.w;
+      Y.x += yr.x; Y.y += yr.y; Y.z += yr.z; Y.w += yr.w;
+      QK += s_red[r][cg][2].x;
+    }
   }
 
   const Tio* v = static_cast<const Tio*>(a.v) + (size_t)bh * D + 4 * cg;
