@@ -470,24 +470,27 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
       const int nn = job - m * (m + 1) / 2;
       const int r = 16 * m + rl, s = 16 * nn + rl;
       f32x4 accA = zero4(), accMT = zero4();
+      // rho_{n+1} = rho_m for the pair (m, m-1): its factor is exactly 1 and
+      // the column base goes to the matrix cores as it is
+      const bool unit = m == nn + 1;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const int cc = 32 * ks + 8 * kg;
-        bf16x8 kr = zero_bf16x8(), qr = zero_bf16x8();
-        float kc[8];
+        bf16x8 kr = zero_bf16x8(), qr = zero_bf16x8(), kcb = zero_bf16x8();
         if (kFullK || cc < K) {
-          float f[8];
           kr = *reinterpret_cast<const bf16x8*>(&s_kh[r][cc]);
           qr = *reinterpret_cast<const bf16x8*>(&s_qh[r][cc]);
-          lds_get8(&s_kcb[s][cc], kc);
-          lds_get8(&s_f[job][cc], f);
+          if (unit) {
+            kcb = *reinterpret_cast<const bf16x8*>(&s_kcb[s][cc]);
+          } else {
+            float kc[8], f[8];
+            lds_get8(&s_kcb[s][cc], kc);
+            lds_get8(&s_f[job][cc], f);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) kc[e] *= f[e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) kc[e] = 0.f;
+            for (int e = 0; e < 8; ++e) kc[e] *= f[e];
+            kcb = pack8(kc);
+          }
         }
-        const bf16x8 kcb = pack8(kc);
         accA = mfma_bf16(kr, kcb, accA);    // A tile: rows r, cols s
         accMT = mfma_bf16(kcb, qr, accMT);  // M^T tile: rows s, cols r
       }
