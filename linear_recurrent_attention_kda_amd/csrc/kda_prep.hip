@@ -416,6 +416,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
     lds_get8(&s_rho[m][c0], rho);
     lds_get8(&s_rho[m + 1][c0], rho1);
     lds_get8(&s_rho[NSUB][c0], alast);
+    // per channel: e^rho and e^{a_last - rho1}; then per element
+    //   e^a = e^rho e^{a - rho},   e^{a_last - a} = e^{a_last - rho1} e^{rho1 - a}
+    // (a is non-increasing, so a factor that underflows stands for a value
+    // that is smaller still)
+    float erho[8], etail[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      erho[e] = __builtin_amdgcn_exp2f(rho[e]);
+      etail[e] = __builtin_amdgcn_exp2f(alast[e] - rho1[e]);
+    }
     float kbar[8][RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -428,12 +438,13 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
       for (int e = 0; e < 8; ++e) {
         const float av = gx[i][e];
         const float f = __builtin_amdgcn_exp2f(av - rho[e]);
-        const float ea = __builtin_amdgcn_exp2f(av);
+        const float ea = erho[e] * f;
+        const float fc = __builtin_amdgcn_exp2f(rho1[e] - av);
         qh[e] = q[e] * f;
         kh[e] = k[e] * f;
-        kc[e] = k[e] * __builtin_amdgcn_exp2f(rho1[e] - av);
+        kc[e] = k[e] * fc;
         qe[e] = q[e] * ea;
-        kbar[e][i] = k[e] * __builtin_amdgcn_exp2f(alast[e] - av);
+        kbar[e][i] = k[e] * (etail[e] * fc);
         kbT[e][i] = bt[i] * k[e] * ea;
         vbT[e][i] = bt[i] * v[e];
       }
