@@ -119,9 +119,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; KDA shards over "
+        print("bench.py measures one GPU only: KDA shards over "
               "(sequence, head) with no communication, so a multi-GPU run "
-              "is one independent copy per GPU (see the design notes). "
+              "is one independent copy of this step per GPU. "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 
