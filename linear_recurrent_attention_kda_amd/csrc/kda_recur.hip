@@ -377,14 +377,6 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
   }
 }
 
-template <typename Tout, int D, int C, int BV, int PF, int NW,
-          bool kCkpt = false>
-hipError_t launch_bv(const PrefillArgs& a, hipStream_t st) {
-  const unsigned blocks = (unsigned)(D / BV) * (unsigned)a.H * (unsigned)a.N;
-  return launch_kernel(recur_kernel<Tout, D, C, BV, PF, NW, kCkpt>,
-                       dim3(blocks), dim3(64 * NW), st, a);
-}
-
 // Slice width.  Wider slices re-read the per-chunk tensors fewer times and
 // do more matrix work per chunk loaded; narrower ones give more workgroups
 // when there are few (sequence, head) pairs.  Measured on MI355X: 96 heads
@@ -397,8 +389,10 @@ inline int pick_bv(int D, int64_t units) {
   }();
   int cus = 256;
   int dev = 0;
-  if (hipGetDevice(&dev) == hipSuccess)
-    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                            dev) != hipSuccess)
+    cus = 256;
   int bv = 16;
   if (D >= 64 && units * (D / 64) >= cus / 2)
     bv = 64;
@@ -410,34 +404,18 @@ inline int pick_bv(int D, int64_t units) {
   return D == 16 ? 16 : bv;
 }
 
-// Register operand sets in flight (2 or 3); KDA_RECUR_PF overrides.
-inline int pick_pf() {
-  static const int forced = [] {
-    const char* e = getenv("KDA_RECUR_PF");
-    return e ? atoi(e) : 0;
-  }();
-  return forced == 3 ? 3 : 2;  // a third operand set measured no faster
-}
-
-// Waves per workgroup (4 or 8); KDA_RECUR_WAVES overrides.
-inline int pick_waves() {
-  static const int forced = [] {
-    const char* e = getenv("KDA_RECUR_WAVES");
-    return e ? atoi(e) : 0;
-  }();
-  return forced == 8 ? 8 : 4;
-}
-
+// Two register operand sets in flight and 4 waves per workgroup: a third
+// set, or 8 waves (also with the outputs' products given to their own
+// waves), measured no faster on MI355X.
 template <typename Tout, int D, int C, int BV>
 hipError_t launch_w(const PrefillArgs& a, hipStream_t st) {
-  // state checkpoints: their own kernel variant, default shape
-  if (a.ckpt_states) return launch_bv<Tout, D, C, BV, 2, 4, true>(a, st);
-  const int pf = pick_pf();
-  if (pick_waves() == 8 && (D / 16) * (BV / 16) >= 8 && (C / 16) * (BV / 16) >= 8)
-    return pf == 2 ? launch_bv<Tout, D, C, BV, 2, 8>(a, st)
-                   : launch_bv<Tout, D, C, BV, 3, 8>(a, st);
-  return pf == 2 ? launch_bv<Tout, D, C, BV, 2, 4>(a, st)
-                 : launch_bv<Tout, D, C, BV, 3, 4>(a, st);
+  const unsigned blocks = (unsigned)(D / BV) * (unsigned)a.H * (unsigned)a.N;
+  // state checkpoints: their own kernel variant
+  return a.ckpt_states
+             ? launch_kernel(recur_kernel<Tout, D, C, BV, 2, 4, true>,
+                             dim3(blocks), dim3(256), st, a)
+             : launch_kernel(recur_kernel<Tout, D, C, BV, 2, 4, false>,
+                             dim3(blocks), dim3(256), st, a);
 }
 
 template <typename Tout, int D, int C>
