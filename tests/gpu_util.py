@@ -1,11 +1,19 @@
 """Helpers for the GPU parity tests: move seeded problems to the device, run
 libkda through its C ABI, run the fp64 oracle on the same values, compare.
 
-Error measure (per independent (sequence, head) slice, maximum over
-slices): max |x - x_ref| / max |x_ref|.  Tolerances: 2e-2 for prefill
-outputs and final states (the prefill path multiplies bf16 operands on the
-matrix cores by design), 1e-4 for the fp32 decode state, 2e-2 for bf16
-decode outputs and 1e-4 for fp32 decode outputs.
+Error measure: max |x - x_ref| / max |x_ref| over a slice, maximum over
+slices.  Final states and decode outputs: one slice per (sequence, head).
+Prefill outputs: one slice per head, over every token of the call.  The
+prefill path multiplies bf16 operands on the matrix cores by design, so its
+error in an output is relative to the magnitudes of the summed terms; a
+sequence of a token or two that starts from a zero state has the output
+(q . k) beta v, and q . k of two unit vectors can nearly vanish, so the
+relative error of such a slice measures the inputs' conditioning, not the
+kernel.  Every output of a head has the same scale whatever its sequence's
+length (the state's size is bounded by the decay), so a wrong or misplaced
+sequence still shows as an error of order one.  Tolerances: 2e-2 for
+prefill outputs and final states, 1e-4 for the fp32 decode state, 2e-2 for
+bf16 decode outputs and 1e-4 for fp32 decode outputs.
 """
 from __future__ import annotations
 
@@ -62,8 +70,15 @@ def slice_rel(x, ref, slice_axes):
     return float(np.max(num / den)) if num.size else 0.0
 
 
-def varlen_o_rel(o, ref, cu):
-    """Per-(sequence, head) relative error of packed outputs [total, H, V]."""
+def prefill_o_rel(o, ref):
+    """Per-head relative error of prefill outputs, packed [total, H, V] or
+    batched [B, T, H, V] (heads on the second-to-last axis)."""
+    return slice_rel(o, ref, (np.ndim(o) - 2,))
+
+
+def worst_sequence_rel(o, ref, cu):
+    """Largest per-(sequence, head) relative error of packed outputs (for
+    the log: it reflects the conditioning of the shortest sequences)."""
     worst = 0.0
     for n in range(len(cu) - 1):
         a, b = int(cu[n]), int(cu[n + 1])
@@ -115,12 +130,13 @@ def check_prefill(p: inputs.Problem, heads=None, tol=PREFILL_TOL, label="",
         % (p.kind, p.H, p.K, p.C, p.tokens, p.dtype))
     o, s = run_prefill_gpu(p, heads, alias_state, scale)
     o_ref, s_ref = run_oracle(p, heads, scale)
-    if p.kind == "varlen":
-        eo = varlen_o_rel(o, o_ref, p.cu_seqlens)
-    else:
-        eo = slice_rel(o, o_ref, (0, 2))
+    eo = prefill_o_rel(o, o_ref)
     es = slice_rel(s, s_ref, (0, 1))
-    log("   o rel err %.3e   final state rel err %.3e" % (eo, es))
+    extra = ""
+    if p.kind == "varlen":
+        extra = "   (worst single sequence %.3e)" % worst_sequence_rel(
+            o, o_ref, p.cu_seqlens)
+    log("   o rel err %.3e   final state rel err %.3e%s" % (eo, es, extra))
     assert eo <= tol, ("output", eo)
     assert es <= tol, ("final state", es)
     return eo, es

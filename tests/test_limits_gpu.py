@@ -1,0 +1,72 @@
+"""GPU parity at the edges of the supported sizes: very many heads (large
+token strides in the packed layout, fp32 inputs), very many short packed
+sequences, a large decode batch, and the longest speculative draft.  Each
+is compared with the fp64 oracle on sampled heads or sequences (heads and
+sequences are independent)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import gpu_available
+from linear_recurrent_attention_kda_amd import inputs, kda
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+import gpu_util as U  # noqa: E402
+
+
+def test_many_heads_fp32_partial_chunk():
+    """4096 heads: one token row is 2 MB of fp32 q, so a 64-token chunk
+    spans 128 MB of each input; T = 130 ends in a partial chunk."""
+    p = inputs.make("prefill", seed=51, B=1, T=130, H=4096, dtype="fp32",
+                    s0=True)
+    U.check_prefill(p, heads=[0, 2047, 4095], label="4096 heads fp32")
+
+
+def test_thousand_short_sequences():
+    rng = np.random.default_rng(52)
+    lengths = rng.integers(0, 40, size=1000).tolist()
+    p = inputs.make("varlen", seed=52, H=2, K=64, V=64, C=16, lengths=lengths)
+    U.check_prefill(p, label="1000 sequences")
+
+
+def test_large_decode_batch():
+    """256 sequences x 96 heads (a 1.6 GB fp32 state), sampled sequences."""
+    p = inputs.make("decode", seed=53, B=256)
+    q, k, v = (U.to_dev(x, p.dtype) for x in (p.q, p.k, p.v))
+    state = U.f32_dev(p.initial_state)
+    o = kda.kda_decode_step(q, k, v, U.f32_dev(p.g), U.f32_dev(p.beta), state)
+    torch.cuda.synchronize()
+    for b in (0, 100, 255):
+        sl = slice(b, b + 1)
+        o_ref, s_ref = oracle.run_decode(p.q[sl], p.k[sl], p.v[sl], p.g[sl],
+                                         p.beta[sl], p.initial_state[sl])
+        es = U.slice_rel(U.host(state[sl]), s_ref, (0, 1))
+        eo = U.slice_rel(U.host(o[sl]), o_ref, (0, 1))
+        U.log("decode B=256 seq %d: o %.3e state %.3e" % (b, eo, es))
+        assert es <= U.DECODE_STATE_TOL and eo <= U.DECODE_O_TOL["bf16"]
+
+
+def test_longest_speculative_draft():
+    """T = 16 draft tokens (the supported maximum), all accepted."""
+    B, T, H, D = 3, 16, 4, 128
+    p = inputs.make("varlen", seed=54, H=H, K=D, V=D, lengths=[T] * B)
+    shp = lambda x: U.to_dev(x.reshape((B, T) + x.shape[1:]),  # noqa: E731
+                             p.dtype)
+    q, k, v = shp(p.q), shp(p.k), shp(p.v)
+    g = U.f32_dev(p.g.reshape((B, T) + p.g.shape[1:]))
+    beta = U.f32_dev(p.beta.reshape(B, T, H))
+    state = U.f32_dev(p.initial_state)
+    o, u = kda.kda_spec_verify(q, k, v, g, beta, state)
+    kda.kda_spec_commit(k, g, u, torch.full((B,), T, dtype=torch.int32,
+                                            device=U.DEV), state)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.run_varlen(p.q, p.k, p.v, p.g, p.beta,
+                                     p.cu_seqlens, p.initial_state)
+    eo = max(U.slice_rel(U.host(o)[b], o_ref[b * T:(b + 1) * T], (1,))
+             for b in range(B))
+    es = U.slice_rel(U.host(state), s_ref, (0, 1))
+    U.log("spec T=16: o %.3e state %.3e" % (eo, es))
+    assert eo <= U.DECODE_O_TOL["bf16"] and es <= U.DECODE_STATE_TOL
