@@ -534,9 +534,13 @@ def cpu_baseline(dp, pp):
     oracle.build(force=False)
     threads = min(16, os.cpu_count() or 1)
     oracle.set_threads(threads)
-    t = time.perf_counter()
-    oracle.run_decode(dp.q, dp.k, dp.v, dp.g, dp.beta, dp.initial_state)
-    dec_s = time.perf_counter() - t
+    # each leg repeats (same inputs, results discarded) until it has run
+    # for a few seconds, so that the rate is not one short noisy sample
+    dec_reps, t = 0, time.perf_counter()
+    while dec_reps == 0 or time.perf_counter() - t < 4.0:
+        oracle.run_decode(dp.q, dp.k, dp.v, dp.g, dp.beta, dp.initial_state)
+        dec_reps += 1
+    dec_s = (time.perf_counter() - t) / dec_reps
     dec_bytes = counts.decode_bytes_per_head(dp.K) * dp.B * dp.H
     # prefill sample: about 96 x 8192 token-heads (the whole 8K-token,
     # 96-head workload; a proportional number of heads of larger ones)
@@ -545,33 +549,34 @@ def cpu_baseline(dp, pp):
     nh = max(1, min(pp.H, (96 * 8192) // max(1, total_tokens)))
     heads = list(range(nh))
     sel = lambda x: x[..., heads, :]  # noqa: E731
-    t = time.perf_counter()
-    if pp.kind == "varlen":
-        oracle.run_varlen(sel(pp.q), sel(pp.k), sel(pp.v), sel(pp.g),
-                          pp.beta[..., heads], pp.cu_seqlens,
-                          None if pp.initial_state is None
-                          else pp.initial_state[:, heads])
-        total = int(pp.cu_seqlens[-1])
-    else:
-        oracle.run_fixed(sel(pp.q), sel(pp.k), sel(pp.v), sel(pp.g),
-                         pp.beta[..., heads],
-                         None if pp.initial_state is None
-                         else pp.initial_state[:, heads])
-        total = pp.B * pp.T
-    pre_s = time.perf_counter() - t
+    s0 = None if pp.initial_state is None else pp.initial_state[:, heads]
+    pre_reps, t = 0, time.perf_counter()
+    while pre_reps == 0 or time.perf_counter() - t < 6.0:
+        if pp.kind == "varlen":
+            oracle.run_varlen(sel(pp.q), sel(pp.k), sel(pp.v), sel(pp.g),
+                              pp.beta[..., heads], pp.cu_seqlens, s0)
+        else:
+            oracle.run_fixed(sel(pp.q), sel(pp.k), sel(pp.v), sel(pp.g),
+                             pp.beta[..., heads], s0)
+        pre_reps += 1
+    pre_s = (time.perf_counter() - t) / pre_reps
+    total = int(pp.cu_seqlens[-1]) if pp.kind == "varlen" else pp.B * pp.T
     pre_tps = total / (pre_s * pp.H / len(heads))
-    log("oracle: decode %.2fs, prefill sample %.2fs" % (dec_s, pre_s))
+    log("oracle: decode %.3fs x %d, prefill sample %.3fs x %d"
+        % (dec_s, dec_reps, pre_s, pre_reps))
     return {
         "value": round(dec_bytes / dec_s / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "whole decode step (64x96 heads, d=128) in fp64; prefill: "
-                  "%d of %d heads over all %d tokens, scaled to all heads"
-                  % (len(heads), pp.H, total),
+        "sample": "whole decode step (%dx%d heads, d=%d) in fp64, mean of "
+                  "%d runs; prefill: %d of %d heads over all %d tokens, "
+                  "scaled to all heads, mean of %d runs"
+                  % (dp.B, dp.H, dp.K, dec_reps, len(heads), pp.H, total,
+                     pre_reps),
         "prefill_tokens_per_s": round(pre_tps, 1),
-        "decode_seconds": round(dec_s, 3),
-        "prefill_sample_seconds": round(pre_s, 3),
+        "decode_seconds": round(dec_s, 4),
+        "prefill_sample_seconds": round(pre_s, 4),
         "cpu_model": cpu_model(),
     }
 
