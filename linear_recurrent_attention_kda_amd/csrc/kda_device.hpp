@@ -213,6 +213,35 @@ namespace kda {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Wait until at most N vector-memory operations of this wave are
+// outstanding (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; the
+// exp and lgkm counters at their maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) |
+                             (15 << 8));
+}
+
+// LDS-direct copies (global_load_lds): lane l's n bytes from src land at
+// lds + n * l (n = 16 or 4), so a wave moves one contiguous block per
+// instruction.  `lds` must be the same for every lane of the wave.
+__device__ __forceinline__ void copy16_to_lds(const char* src, char* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+__device__ __forceinline__ void copy4_to_lds(const char* src, char* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
+}
+
+// Workgroup barrier without the memory fences of __syncthreads(), for a wave
+// that makes its LDS writes visible by waiting on its own counters (the
+// empty asm statements keep the compiler from moving memory accesses across).
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Token range [bos, eos) of sequence n, clamped into [0, total_T] so that an
 // invalid cu_seqlens can never index outside the packed tensors.
 __device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int n,

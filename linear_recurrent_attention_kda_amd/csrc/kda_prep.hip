@@ -201,6 +201,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
   Raw8<Tin> rq[RPT], rk[RPT], rv[RPT];
   if (!kPro) {
     if (active) {
+      // g and beta first: loads complete in order, so the decay scan waits
+      // only for them while q, k and v are still arriving
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const uint32_t row = (uint32_t)((r0 + i) * H);
@@ -210,10 +212,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
         gx[i][2] = __uint_as_float(g0.z); gx[i][3] = __uint_as_float(g0.w);
         gx[i][4] = __uint_as_float(g1.x); gx[i][5] = __uint_as_float(g1.y);
         gx[i][6] = __uint_as_float(g1.z); gx[i][7] = __uint_as_float(g1.w);
+      }
+#pragma unroll
+      for (int i = 0; i < RPT; ++i)
+        bt[i] = buffer_load_f32(Rb, (uint32_t)((r0 + i) * H) * 4);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const uint32_t row = (uint32_t)((r0 + i) * H);
         rq[i].load_buf(Rq, (row * K + c0) * sizeof(Tin));
         rk[i].load_buf(Rk, (row * K + c0) * sizeof(Tin));
         rv[i].load_buf(Rv, (row * V + c0) * sizeof(Tin));
-        bt[i] = buffer_load_f32(Rb, row * 4);
       }
     } else {
 #pragma unroll

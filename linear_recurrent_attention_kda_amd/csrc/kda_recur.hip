@@ -377,6 +377,298 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Streamed variant: a fifth wave copies each chunk's operands from the
+// workspace into one of two LDS buffers with LDS-direct loads
+// (global_load_lds: every lane's 16 bytes land at the buffer offset plus
+// 16 x lane, so one instruction moves one contiguous 1 KB fragment), and
+// the four compute waves read them with 16-byte LDS reads.  The compute
+// waves then issue no global loads at all: the address unit's back-pressure
+// and the loads' latency fall on the loader wave.
+//
+// Operands of chunk ci are split in two parts by when they are consumed:
+//   part A: W, Q^ and this slice's U~^T   (read before the mid-chunk barrier)
+//   part B: K-bar^T, M and gamma           (read after it)
+// With X_ci / Y_ci the chunk's first / mid-chunk barrier, the loader issues
+// part B of chunk ci + 1 after X_ci (its buffer's previous part B, chunk
+// ci - 1's, was consumed before X_ci) and part A of chunk ci + 2 after Y_ci
+// (chunk ci's part A was consumed before Y_ci), then waits until only that
+// last part A is outstanding, so that both parts of chunk ci + 1 have landed
+// before X_ci+1.  Loads complete in order for the counter, so one wait
+// with the count of part A's instructions does this.
+template <int D, int C, int BV>
+struct OpBuf {
+  static constexpr int MT = C / 16, KST = D / 32, CST = C / 32, KT = D / 16;
+  static constexpr int JT = BV / 16;
+  static constexpr int W = 0;                          // MT*KST fragments
+  static constexpr int QH = W + MT * KST * 1024;       // MT*KST fragments
+  static constexpr int KB = QH + MT * KST * 1024;      // KT*CST fragments
+  static constexpr int M = KB + KT * CST * 1024;       // MT*CST fragments
+  static constexpr int U = M + MT * CST * 1024;        // JT*MT of 512 B
+  static constexpr int G = U + JT * MT * 512;          // D floats
+  static constexpr int BYTES = G + D * 4;
+  static constexpr int NA = 2 * MT * KST + JT * MT / 2;  // part A copies
+  static_assert(D % 32 == 0 && C % 32 == 0 && (JT * MT) % 2 == 0 &&
+                D % 64 == 0, "streamed operand layout");
+  static_assert(NA <= 63, "one counter wait covers part A");
+};
+
+template <typename Tout, int D, int C, int BV, bool kCkpt>
+__global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
+  constexpr int NW = 4;                    // compute waves; wave 4 loads
+  constexpr int K = D, V = D;
+  constexpr int NVT = V / BV;
+  constexpr int KT = K / 16, JT = BV / 16;
+  constexpr int NST = KT * JT;
+  constexpr int SPW = NST / NW;
+  constexpr int MT = C / 16;
+  constexpr int NUT = MT * JT;
+  constexpr int UPW = NUT / NW;
+  constexpr int NCT = SPW >= JT ? SPW / JT : 1;
+  constexpr int KSTEPS = K / 32, CSTEPS = C / 32;
+  constexpr int SP = K + 8, UP = C + 8;
+  using OB = OpBuf<D, C, BV>;
+  static_assert(NUT % NW == 0 && NST % NW == 0 && UPW <= JT &&
+                (SPW % JT == 0 || SPW < JT), "wave tiling");
+  static_assert(2 * OB::BYTES + (BV * SP + BV * UP) * 2 <= 160 * 1024,
+                "LDS budget");
+
+  __shared__ __attribute__((aligned(16))) bf16 s_SbT[BV][SP];
+  __shared__ __attribute__((aligned(16))) bf16 s_UbT[BV][UP];
+  __shared__ __attribute__((aligned(1024))) char s_ops[2][OB::BYTES];
+
+  const unsigned total = gridDim.x;
+  unsigned bid = blockIdx.x;
+  if ((total & 7u) == 0u) bid = (bid & 7u) * (total >> 3) + (bid >> 3);
+  const int vt = bid % NVT;
+  const int h = (bid / NVT) % a.H;
+  const int n = bid / (NVT * a.H);
+  const int j0 = vt * BV;
+  const int H = a.H;
+
+  int64_t bos, eos;
+  seq_bounds(a, n, bos, eos);
+  const WsLayout lay = WsLayout::make(C, K, V);
+  const int64_t nchunks = (eos - bos + C - 1) / C;
+  const char* ws_head = a.ws + (size_t)h * a.nslots * lay.block_bytes;
+  auto chunk_ptr = [&](int64_t ci) {
+    ci = ci < nchunks ? ci : nchunks - 1;  // past the end: a harmless reload
+    const int64_t slot = (bos + ci * C) / C + n;
+    return ws_head + (size_t)slot * lay.block_bytes;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  if (wave == NW) {
+    // ---- loader wave --------------------------------------------------
+    auto copy1k = [&](const char* src, int dst) {
+      copy16_to_lds(src + 16 * lane, &s_ops[0][0] + dst);
+    };
+    auto issue_a = [&](int64_t ci, int b) {
+      const char* blk = chunk_ptr(ci);
+      const int base = b * OB::BYTES;
+#pragma unroll
+      for (int f = 0; f < 2 * OB::MT * OB::KST; ++f)
+        copy1k(blk + lay.off_W + 1024 * f, base + OB::W + 1024 * f);
+      const char* ut = blk + lay.off_UtT + (size_t)(j0 / 16) * lay.mt * 512;
+#pragma unroll
+      for (int f = 0; f < JT * MT / 2; ++f)
+        copy1k(ut + 1024 * f, base + OB::U + 1024 * f);
+    };
+    auto issue_b = [&](int64_t ci, int b) {
+      const char* blk = chunk_ptr(ci);
+      const int base = b * OB::BYTES;
+#pragma unroll
+      for (int f = 0; f < KT * CSTEPS; ++f)
+        copy1k(blk + lay.off_KbT + 1024 * f, base + OB::KB + 1024 * f);
+#pragma unroll
+      for (int f = 0; f < MT * CSTEPS; ++f)
+        copy1k(blk + lay.off_M + 1024 * f, base + OB::M + 1024 * f);
+#pragma unroll
+      for (int f = 0; f < D / 64; ++f)  // gamma: 256 B per instruction
+        copy4_to_lds(blk + lay.off_gamma + 256 * f + 4 * lane,
+                       &s_ops[0][0] + base + OB::G + 256 * f);
+    };
+    if (nchunks > 0) {
+      issue_a(0, 0);
+      issue_b(0, 0);
+      issue_a(1, 1);
+      wait_vmcnt<OB::NA>();                 // chunk 0 has landed
+      for (int64_t ci = 0; ci < nchunks; ++ci) {
+        const int b = (int)(ci & 1);
+        raw_barrier();                      // X_ci
+        issue_b(ci + 1, b ^ 1);
+        raw_barrier();                      // Y_ci
+        issue_a(ci + 2, b);
+        wait_vmcnt<OB::NA>();               // chunk ci + 1 has landed
+      }
+      wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is gone
+    }
+    return;
+  }
+
+  // ---- compute waves ----------------------------------------------------
+  const int rl = lane & 15, kg = lane >> 4;
+  const int u0 = wave * UPW;
+  const int mrow = u0 / JT;
+  const int s0t = wave * SPW;
+  const int ct0 = s0t / JT;
+
+  f32x4 S[SPW];
+  const size_t sbase = ((size_t)n * H + h) * (size_t)K * V;
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int t = s0t + i;
+    const int ct = t / JT, jt = t % JT;
+    S[i] = zero4();
+    if (a.initial_state) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        S[i][e] = a.initial_state[sbase + (size_t)(16 * ct + 4 * kg + e) * V +
+                                  j0 + 16 * jt + rl];
+    }
+    bf16x4 sb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sb[e] = (bf16)S[i][e];
+    *reinterpret_cast<bf16x4*>(&s_SbT[16 * jt + rl][16 * ct + 4 * kg]) = sb;
+  }
+
+  Tout* o = static_cast<Tout*>(a.o);
+  for (int64_t ci = 0; ci < nchunks; ++ci) {
+    const char* ob = &s_ops[ci & 1][0];
+    const int64_t t0 = bos + ci * C;
+    const int L = (eos - t0) < C ? (int)(eos - t0) : C;
+    const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(
+        o + (t0 * H + h) * (int64_t)V + j0,
+        (uint32_t)(((int64_t)(L - 1) * H * V + BV) * sizeof(Tout)));
+    __syncthreads();  // X_ci: S^T copy complete, U^T free, operands landed
+
+    // U = U~ - W S,  O^T = S^T Q^^T
+    bf16x8 w[KSTEPS], qh[KSTEPS], sbf[UPW][KSTEPS];
+    uint2 ut[UPW];
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      w[kk] = *reinterpret_cast<const bf16x8*>(
+          ob + OB::W + ((mrow * KSTEPS + kk) * 64 + lane) * 16);
+      qh[kk] = *reinterpret_cast<const bf16x8*>(
+          ob + OB::QH + ((mrow * KSTEPS + kk) * 64 + lane) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      const int jt = (u0 + i) % JT;
+      ut[i] = *reinterpret_cast<const uint2*>(
+          ob + OB::U + ((jt * MT + mrow) * 64 + lane) * 8);
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        sbf[i][kk] = *reinterpret_cast<const bf16x8*>(
+            &s_SbT[16 * jt + rl][32 * kk + 8 * kg]);
+    }
+    f32x4 Ot[UPW];
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      const int jt = (u0 + i) % JT;
+      f32x4 wsacc = zero4();
+      Ot[i] = zero4();
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        wsacc = mfma_bf16(w[kk], sbf[i][kk], wsacc);
+        Ot[i] = mfma_bf16(sbf[i][kk], qh[kk], Ot[i]);
+      }
+      const bf16x4 u4 = __builtin_bit_cast(bf16x4, ut[i]);
+      bf16x4 ub;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ub[e] = (bf16)((float)u4[e] - wsacc[e]);
+      *reinterpret_cast<bf16x4*>(&s_UbT[16 * jt + rl][16 * mrow + 4 * kg]) = ub;
+    }
+    __syncthreads();  // Y_ci: U^T complete
+
+    bf16x8 ubf[JT][CSTEPS], mf[CSTEPS], kb[NCT][CSTEPS];
+    float4 gm[NCT];
+#pragma unroll
+    for (int cs = 0; cs < CSTEPS; ++cs) {
+      mf[cs] = *reinterpret_cast<const bf16x8*>(
+          ob + OB::M + ((mrow * CSTEPS + cs) * 64 + lane) * 16);
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt)
+        ubf[jt][cs] = *reinterpret_cast<const bf16x8*>(
+            &s_UbT[16 * jt + rl][32 * cs + 8 * kg]);
+    }
+#pragma unroll
+    for (int lc = 0; lc < NCT; ++lc) {
+      const int ct = ct0 + lc;
+#pragma unroll
+      for (int cs = 0; cs < CSTEPS; ++cs)
+        kb[lc][cs] = *reinterpret_cast<const bf16x8*>(
+            ob + OB::KB + ((ct * CSTEPS + cs) * 64 + lane) * 16);
+      gm[lc] = *reinterpret_cast<const float4*>(ob + OB::G +
+                                                (16 * ct + 4 * kg) * 4);
+    }
+
+    // O^T += U^T M^T; store O (rows >= L fall outside the buffer: dropped)
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      const int jt = (u0 + i) % JT;
+#pragma unroll
+      for (int cs = 0; cs < CSTEPS; ++cs)
+        Ot[i] = mfma_bf16(ubf[jt][cs], mf[cs], Ot[i]);
+      const int r = 16 * mrow + rl;
+      buffer_store4(o, orsrc,
+                    (uint32_t)(((int64_t)r * H * V + 16 * jt + 4 * kg) *
+                               sizeof(Tout)),
+                    Ot[i], a.scale);
+    }
+
+    // S <- diag(gamma) S + K-bar^T U
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      constexpr bool kRows = SPW >= JT;
+      const int t = s0t + i;
+      const int lc = kRows ? i / JT : 0;
+      const int jt = kRows ? i % JT : t % JT;
+      const int ct = ct0 + lc;
+      const float4 g4 = gm[lc];
+      S[i][0] *= g4.x; S[i][1] *= g4.y; S[i][2] *= g4.z; S[i][3] *= g4.w;
+#pragma unroll
+      for (int cs = 0; cs < CSTEPS; ++cs)
+        S[i] = mfma_bf16(kb[lc][cs], ubf[jt][cs], S[i]);
+      bf16x4 sb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sb[e] = (bf16)S[i][e];
+      *reinterpret_cast<bf16x4*>(&s_SbT[16 * jt + rl][16 * ct + 4 * kg]) = sb;
+    }
+    // state checkpoint after this chunk (uniform over the workgroup)
+    if (kCkpt) {
+      const int64_t p = (ci + 1) * C;
+      if (p % a.ckpt_every == 0 && p <= eos - bos) {
+        const int64_t cslot = (bos + p) / a.ckpt_every - 1;
+        float* dst = a.ckpt_states + ((size_t)cslot * H + h) * (size_t)K * V;
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+          const int t = s0t + i;
+          const int ct = t / JT, jt = t % JT;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dst[(size_t)(16 * ct + 4 * kg + e) * V + j0 + 16 * jt + rl] =
+                S[i][e];
+        }
+      }
+    }
+  }
+
+  if (a.final_state) {
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      const int t = s0t + i;
+      const int ct = t / JT, jt = t % JT;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        a.final_state[sbase + (size_t)(16 * ct + 4 * kg + e) * V + j0 +
+                      16 * jt + rl] = S[i][e];
+    }
+  }
+}
+
 // Slice width.  Wider slices re-read the per-chunk tensors fewer times and
 // do more matrix work per chunk loaded; narrower ones give more workgroups
 // when there are few (sequence, head) pairs.  Measured on MI355X: 96 heads
@@ -407,9 +699,29 @@ inline int pick_bv(int D, int64_t units) {
 // Two register operand sets in flight and 4 waves per workgroup: a third
 // set, or 8 waves (also with the outputs' products given to their own
 // waves), measured no faster on MI355X.
+// Variant choice for D = 128, C = 64.  Measured on MI355X: the streamed
+// variant runs the 96-head prefill workload (64-wide slices) in 287 us
+// against 301 us, and the 32-head long workload (16-wide slices) 4 % slower.
+// KDA_RECUR_STREAM=0 / 1 forces the choice for tuning sweeps.
+inline bool use_stream(int bv) {
+  static const int forced = [] {
+    const char* e = getenv("KDA_RECUR_STREAM");
+    return e ? (atoi(e) != 0 ? 1 : 0) : -1;
+  }();
+  return forced >= 0 ? forced == 1 : bv == 64;
+}
+
 template <typename Tout, int D, int C, int BV>
 hipError_t launch_w(const PrefillArgs& a, hipStream_t st) {
   const unsigned blocks = (unsigned)(D / BV) * (unsigned)a.H * (unsigned)a.N;
+  if constexpr (D == 128 && C == 64 && BV <= 64) {
+    if (use_stream(BV))
+      return a.ckpt_states
+                 ? launch_kernel(recur_stream_kernel<Tout, D, C, BV, true>,
+                                 dim3(blocks), dim3(320), st, a)
+                 : launch_kernel(recur_stream_kernel<Tout, D, C, BV, false>,
+                                 dim3(blocks), dim3(320), st, a);
+  }
   // state checkpoints: their own kernel variant
   return a.ckpt_states
              ? launch_kernel(recur_kernel<Tout, D, C, BV, 2, 4, true>,
