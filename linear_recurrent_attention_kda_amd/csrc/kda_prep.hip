@@ -111,8 +111,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
   constexpr int NUP = NSUB * (NSUB - 1) / 2;    // (m, n > m): M is zero there
   constexpr int NJOBW = (NPAIR + NUP + NW - 1) / NW;  // jobs per wave
   constexpr int KT = K / 16, VT = V / 16;
-  constexpr int NTILE = NSUB * (KT + VT);  // W^T and U~ output tiles
-  constexpr int TPW = (NTILE + NW - 1) / NW;
   constexpr int RP = D + 8;  // bf16 row stride of the [C][D] row operands
   constexpr int TP = C + 8;  // bf16 row stride of the [D][C] transposes
   constexpr int AP = C + 4;  // fp32 row stride of A and INV
@@ -163,7 +161,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
   if (!it.valid) return;  // past the end of a packed sequence (uniform)
 
   const int H = a.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform across the wave: read it into a scalar
+  // register so that branches on it are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rl = lane & 15, kg = lane >> 4;
   const int cg = tid % CGN, r0 = (tid / CGN) * RPT, c0 = 8 * cg;
   const bool active = kFullSt || tid < NST;
@@ -608,35 +609,80 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
   __syncthreads();
 
   // ---- 5. W = INV (beta k e^a) (row-major, via W^T tiles) and
-  //         U~ = INV (beta v) (stored transposed) ----------------------------
+  //         U~ = INV (beta v) (stored transposed).  Wave w takes the W and
+  //         U~ column tiles w, w + NW, ... of every 16-row tile m; m, the
+  //         tile kind and the number of 32-column steps are compile-time,
+  //         so each m's operand reads, products and stores issue as one
+  //         batch.  INV is zero above its diagonal blocks, so row tile m
+  //         needs columns s < 16 (m + 1) only. ---------------------------------
+  constexpr int WPW = (KT + NW - 1) / NW;  // W column tiles per wave and m
+  constexpr int UPW = (VT + NW - 1) / NW;  // U~ column tiles per wave and m
+  constexpr int CSMAX = (C + 31) / 32;
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int t = wave + NW * i;  // interleaved: every wave sees every m
-    if (NTILE % NW == 0 || t < NTILE) {
-      const int m = t / (KT + VT), ct = t % (KT + VT);
-      const bool isW = ct < KT;
-      const int col = 16 * (isW ? ct : ct - KT) + rl;
-      const int r = 16 * m + rl;
-      const int csteps = (16 * (m + 1) + 31) / 32;
-      f32x4 acc = zero4();
-      for (int cs = 0; cs < csteps; ++cs) {
-        const int s0 = 32 * cs + 8 * kg;
-        bf16x8 iv = zero_bf16x8(), bv = zero_bf16x8();
-        if (s0 < C) {
-          iv = *reinterpret_cast<const bf16x8*>(&s_invb[r][s0]);
-          bv = *reinterpret_cast<const bf16x8*>(
-              isW ? &s_kbT[col][swz(col, s0)] : &s_vbT[col][swz(col, s0)]);
+  for (int m = 0; m < NSUB; ++m) {
+    const int r = 16 * m + rl;
+    const int csteps = (16 * (m + 1) + 31) / 32;
+    bf16x8 iv[CSMAX];
+#pragma unroll
+    for (int cs = 0; cs < CSMAX; ++cs) {
+      const int s0 = 32 * cs + 8 * kg;
+      iv[cs] = zero_bf16x8();
+      if (cs < csteps && (C % 32 == 0 || s0 < C))
+        iv[cs] = *reinterpret_cast<const bf16x8*>(&s_invb[r][s0]);
+    }
+    f32x4 accW[WPW], accU[UPW];
+#pragma unroll
+    for (int x = 0; x < WPW; ++x) {
+      const int ct = wave + NW * x, col = 16 * ct + rl;
+      accW[x] = zero4();
+      if (KT % NW == 0 || ct < KT) {
+#pragma unroll
+        for (int cs = 0; cs < CSMAX; ++cs) {
+          const int s0 = 32 * cs + 8 * kg;
+          if (cs < csteps) {
+            bf16x8 bv = zero_bf16x8();
+            if (C % 32 == 0 || s0 < C)
+              bv = *reinterpret_cast<const bf16x8*>(&s_kbT[col][swz(col, s0)]);
+            accW[x] = mfma_bf16(bv, iv[cs], accW[x]);  // W^T: rows c, cols r
+          }
         }
-        acc = isW ? mfma_bf16(bv, iv, acc)   // W^T tile: rows c, cols r
-                  : mfma_bf16(iv, bv, acc);  // U~ tile: rows r, cols j
       }
-      bf16x4 ov;
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ov[e] = (bf16)acc[e];
-      if (isW) {
+    for (int x = 0; x < UPW; ++x) {
+      const int jt = wave + NW * x, col = 16 * jt + rl;
+      accU[x] = zero4();
+      if (VT % NW == 0 || jt < VT) {
+#pragma unroll
+        for (int cs = 0; cs < CSMAX; ++cs) {
+          const int s0 = 32 * cs + 8 * kg;
+          if (cs < csteps) {
+            bf16x8 bv = zero_bf16x8();
+            if (C % 32 == 0 || s0 < C)
+              bv = *reinterpret_cast<const bf16x8*>(&s_vbT[col][swz(col, s0)]);
+            accU[x] = mfma_bf16(iv[cs], bv, accU[x]);  // U~: rows r, cols j
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < WPW; ++x) {
+      const int ct = wave + NW * x;
+      if (KT % NW == 0 || ct < KT) {
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = (bf16)accW[x][e];
         *reinterpret_cast<bf16x4*>(
             gW + WsLayout::frag16(r, 16 * ct + 4 * kg, lay.kst)) = ov;
-      } else {
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < UPW; ++x) {
+      const int jt = wave + NW * x, col = 16 * jt + rl;
+      if (VT % NW == 0 || jt < VT) {
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = (bf16)accU[x][e];
         *reinterpret_cast<bf16x4*>(
             gUtT + WsLayout::frag_ut(col, 16 * m + 4 * kg, lay.mt)) = ov;
       }
