@@ -410,13 +410,24 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
   //         (workspace), row operands and column base (LDS), beta k e^a and
   //         beta v kept for stage 4 ------------------------------------------
   // factor of tile pair p = (m, n <= m), p = m (m + 1) / 2 + n:
-  // e^{rho_m - rho_{n+1}} per channel
-  for (int e = tid; e < NPAIR * D; e += NT) {
-    const int p = e / D, c = e % D;
-    int m = 0;
-    while ((m + 1) * (m + 2) / 2 <= p) ++m;
-    const int nn = p - m * (m + 1) / 2;
-    s_f[p][c] = __builtin_amdgcn_exp2f(s_rho[m][c] - s_rho[nn + 1][c]);
+  // e^{rho_m - rho_{n+1}} per channel.  Thread tid computes channel tid % D
+  // of the pairs p = tid / D (mod NT / D); the adjacent pairs (m, m - 1)
+  // have factor 1 and are never read.  For D >= 64 the pair split is
+  // uniform per wave.
+  {
+    constexpr int PG = NT / D;  // pair groups
+    static_assert(NT % D == 0, "pair factor split");
+    const int c = tid % D;
+    const int grp = D >= kWave ? wave / (D / kWave) : tid / D;
+#pragma unroll
+    for (int m = 0; m < NSUB; ++m) {
+#pragma unroll
+      for (int nn = 0; nn <= m; ++nn) {
+        const int p = m * (m + 1) / 2 + nn;
+        if (nn + 1 != m && p % PG == grp)
+          s_f[p][c] = __builtin_amdgcn_exp2f(s_rho[m][c] - s_rho[nn + 1][c]);
+      }
+    }
   }
   float kbT[8][RPT], vbT[8][RPT];
   if (active) {
