@@ -41,6 +41,20 @@ struct ChunkOps {
   float4 gm[NCT];                 // gamma for the 4 state rows of the lane
 };
 
+// XCD-aware block id.  Workgroup b runs on XCD b % 8 (round-robin
+// dispatch).  Logical id = pair * nvt + slice, pair = sequence * H + head.
+// The slices of one (sequence, head) pair run on one XCD and share its L2,
+// and the pairs are dealt to the XCDs in turn (pair p on XCD p % 8), so every
+// XCD gets the same share of every sequence, whatever the sequence lengths.
+// Without a multiple of 8 pairs the ids are used as they are.
+__device__ __forceinline__ unsigned xcd_logical_id(unsigned b, unsigned total,
+                                                   unsigned nvt) {
+  const unsigned pairs = total / nvt;
+  if ((pairs & 7u) != 0u) return b;
+  const unsigned x = b & 7u, k = b >> 3;
+  return (x + 8u * (k / nvt)) * nvt + k % nvt;
+}
+
 template <typename Tout, int D, int C, int BV, int PF, int NW, bool kCkpt>
 __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
   constexpr int K = D, V = D;
@@ -62,10 +76,7 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 s_SbT[BV][SP];  // S^T, bf16
   __shared__ __attribute__((aligned(16))) bf16 s_UbT[BV][UP];  // U^T, bf16
 
-  // XCD-aware block id: logical ids [x * per, (x + 1) * per) run on XCD x.
-  const unsigned total = gridDim.x;
-  unsigned bid = blockIdx.x;
-  if ((total & 7u) == 0u) bid = (bid & 7u) * (total >> 3) + (bid >> 3);
+  const unsigned bid = xcd_logical_id(blockIdx.x, gridDim.x, NVT);
   const int vt = bid % NVT;
   const int h = (bid / NVT) % a.H;
   const int n = bid / (NVT * a.H);
@@ -437,9 +448,7 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 s_UbT[BV][UP];
   __shared__ __attribute__((aligned(1024))) char s_ops[2][OB::BYTES];
 
-  const unsigned total = gridDim.x;
-  unsigned bid = blockIdx.x;
-  if ((total & 7u) == 0u) bid = (bid & 7u) * (total >> 3) + (bid >> 3);
+  const unsigned bid = xcd_logical_id(blockIdx.x, gridDim.x, NVT);
   const int vt = bid % NVT;
   const int h = (bid / NVT) % a.H;
   const int n = bid / (NVT * a.H);
