@@ -357,7 +357,7 @@ def main(argv=None):
             "mfma_util_frac": round(pre_flops / pre_s / 1e12 /
                                     counts.BF16_MFMA_PEAK_TFLOPS, 4),
             "roofline": {
-                "kernels": "prep_kernel + recur_stream_kernel (one library call)",
+                "kernels": "prep_kernel + recurrence kernel (one library call)",
                 "bound": "hbm",
                 "achieved": round(pre_bytes_pages / pre_s / 1e9, 2),
                 "peak": counts.HBM_PEAK_GBPS,
