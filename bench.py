@@ -406,25 +406,30 @@ def time_spec(T, dp, states, dev, stream, ev):
                           for x in (q, k, v, g, beta))
     od = torch.empty((B, H, dp.V), dtype=torch.bfloat16, device=dev)
     n = 20
-    rec = []
-    for i in range(n + 3):
-        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
-        st = states[i % 3]
+
+    def timed(fn):
+        # n launches back to back between two events (the queue never
+        # drains, so host-side gaps do not enter), states rotated so that
+        # the 402 MB state is not served from the Infinity Cache
+        for i in range(3):
+            fn(i)
+        e0, e1 = ev(), ev()
         e0.record(stream)
-        kda.kda_spec_verify(q, k, v, g, beta, st, o=o, u=u)
+        for i in range(n):
+            fn(i)
         e1.record(stream)
-        kda.kda_spec_commit(k, g, u, acc, st)
-        e2.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ver = timed(lambda i: kda.kda_spec_verify(q, k, v, g, beta, states[i % 3],
+                                              o=o, u=u))
+    com = timed(lambda i: kda.kda_spec_commit(k, g, u, acc, states[i % 3]))
+
+    def steps(i):
         for t in range(T):
             kda.kda_decode_step(qs[t], ks[t], vs[t], gs[t], bs[t],
-                                states[(i + 1) % 3], o=od)
-        e3.record(stream)
-        rec.append((e0, e1, e2, e3))
-    torch.cuda.synchronize()
-    rec = rec[3:]
-    ver = float(np.mean([a.elapsed_time(b) for a, b, _, _ in rec]))
-    com = float(np.mean([b.elapsed_time(c) for _, b, c, _ in rec]))
-    dec = float(np.mean([c.elapsed_time(d) for _, _, c, d in rec]))
+                                states[i % 3], o=od)
+    dec = timed(steps)
     per_head = dp.K * dp.V * 4
     log("spec T=%d: verify %.4f ms, commit %.4f ms, %d decode steps %.4f ms"
         % (T, ver, com, T, dec))
@@ -499,21 +504,26 @@ def time_epilogue(po, dq, dk, dv, dg, dbeta, states, dev, stream, ev):
     for _ in range(n):
         kda.kda_output_norm_gate(po, z, w, y=y)
     a1.record(stream)
-    rec = []
-    for i in range(n + 3):
-        e0, e1, e2 = ev(), ev(), ev()
-        e0.record(stream)
-        kda.kda_decode_step_gated(dq, dk, dv, dg, dbeta, states[i % 3], zd, w)
-        e1.record(stream)
-        kda.kda_decode_step(dq, dk, dv, dg, dbeta, states[(i + 1) % 3])
-        e2.record(stream)
-        rec.append((e0, e1, e2))
     torch.cuda.synchronize()
     epi_ms = a0.elapsed_time(a1) / n
     nbytes = 3 * po.numel() * po.element_size()
-    rec = rec[3:]
-    gated = float(np.mean([a.elapsed_time(b) for a, b, _ in rec]))
-    plain = float(np.mean([b.elapsed_time(c) for _, b, c in rec]))
+
+    def timed(fn):
+        # back-to-back launches on rotating states (see time_spec)
+        for i in range(3):
+            fn(i)
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    gated = timed(lambda i: kda.kda_decode_step_gated(
+        dq, dk, dv, dg, dbeta, states[i % 3], zd, w))
+    plain = timed(lambda i: kda.kda_decode_step(dq, dk, dv, dg, dbeta,
+                                                states[i % 3]))
     log("epilogue: standalone %.4f ms; decode gated %.4f ms vs plain %.4f ms"
         % (epi_ms, gated, plain))
     return {

@@ -99,7 +99,7 @@ __device__ __forceinline__ void store_bf16xn(bf16* p, const float (&x)[N]) {
 constexpr int kConvTaps = 4;
 
 template <typename Tin, int D, int C, bool kPro>
-__global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
+__device__ __forceinline__ void prep_body(const PrefillArgs& a) {
   constexpr int NT = 256, NW = NT / kWave;  // threads, waves
   constexpr int K = D, V = D;
   constexpr int NSUB = C / 16;              // 16-row sub-tiles per chunk
@@ -701,15 +701,27 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
   }
 }
 
+template <typename Tin, int D, int C>
+__global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a) {
+  prep_body<Tin, D, C, false>(a);
+}
+// The prologue variant is capped at 256 registers, so that two workgroups
+// share a compute unit as the LDS footprint allows.
+template <typename Tin, int D, int C>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void prep_pro_kernel(PrefillArgs a) {
+  prep_body<Tin, D, C, true>(a);
+}
+
 // One workgroup per (sequence, chunk, head) item; items past the end of a
 // packed sequence exit at once.
 template <typename Tin, int D, int C>
 hipError_t launch(const PrefillArgs& a, hipStream_t st) {
   const int64_t items = (int64_t)a.N * a.max_chunks * a.H;
   if (a.conv_w)
-    return launch_kernel(prep_kernel<Tin, D, C, true>, dim3((unsigned)items),
+    return launch_kernel(prep_pro_kernel<Tin, D, C>, dim3((unsigned)items),
                          dim3(256), st, a);
-  return launch_kernel(prep_kernel<Tin, D, C, false>, dim3((unsigned)items),
+  return launch_kernel(prep_kernel<Tin, D, C>, dim3((unsigned)items),
                        dim3(256), st, a);
 }
 
