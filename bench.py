@@ -12,7 +12,11 @@ Prints ONE JSON line.  `value` is the decode step's state throughput in GB/s
 (8 * d^2 bytes per head and token, the fp32 state read and written once:
 "Kimi K3: The Manos, The Mythos, The Legendos", section "Complexity
 analysis"); the prefill's tokens/s, FLOP and byte rates ride in the same
-line.  Kernel durations come from HIP events on the stream the kernels run
+line.  The prefill runs as its two stages (kda_prefill_varlen_prep, then
+kda_prefill_varlen_recur), so that each of the step's three kernels is timed
+on its own; `kernels` gives each one's algorithmic HBM rate against the
+peak, and `roofline` repeats the one that takes the largest share of the
+step.  Kernel durations come from HIP events on the stream the kernels run
 on.  Decode rotates three state buffers so that consecutive steps never
 find the state in the 256 MB Infinity Cache.
 
@@ -164,16 +168,19 @@ def main(argv=None):
         po = torch.empty((pp.B, pp.T, pp.H, pp.V), dtype=pq.dtype, device=dev)
     pfs = torch.empty((nseq, pp.H, pp.K, pp.V), dtype=torch.float32,
                       device=dev)
+    # the prefill runs as its two stages (chunk prep, then the recurrence)
+    # on packed sequences, so that each kernel is timed on its own; for one
+    # or more sequences of equal length this is exactly kda_prefill_chunked
+    if pp.kind != "varlen":
+        cu = torch.arange(nseq + 1, dtype=torch.int32, device=dev) * pp.T
+        maxlen = pp.T
+    pq_, pk_, pv_ = (x.reshape(total, pp.H, -1) for x in (pq, pk, pv))
+    pg_, pbeta_ = pg.reshape(total, pp.H, -1), pbeta.reshape(total, pp.H)
+    po_ = po.reshape(total, pp.H, pp.V)
     ck = None
     if args.ckpt_every:
-        if pp.kind != "varlen":
-            cu = torch.arange(nseq + 1, dtype=torch.int32, device=dev) * pp.T
-            maxlen = pp.T
         ck = torch.zeros((total // args.ckpt_every, pp.H, pp.K, pp.V),
                          dtype=torch.float32, device=dev)
-        pq_, pk_, pv_ = (x.reshape(total, pp.H, -1) for x in (pq, pk, pv))
-        pg_, pbeta_ = pg.reshape(total, pp.H, -1), pbeta.reshape(total, pp.H)
-        po_ = po.reshape(total, pp.H, pp.V)
     ws = kda.workspace_for(nseq, total, pp.H, pp.K, pp.V, pp.C, dev)
     calib = None
     if args.calib_copy_mib:
@@ -184,20 +191,22 @@ def main(argv=None):
 
     stream = torch.cuda.current_stream(dev)
 
-    def prefill():
+    def prefill(mid=None):
+        """The prefill; `mid` (an event) is recorded between its two
+        kernels.  With state checkpoints it is one library call."""
         if ck is not None:
             kda.kda_prefill_varlen_ckpt(pq_, pk_, pv_, pg_, pbeta_, cu, maxlen,
                                         ps0, ckpt_every=args.ckpt_every,
                                         chunk_size=pp.C, final_state=pfs,
                                         o=po_, ckpt_states=ck, workspace=ws)
-        elif pp.kind == "varlen":
-            kda.kda_prefill_varlen(pq, pk, pv, pg, pbeta, cu, maxlen, ps0,
-                                   chunk_size=pp.C, final_state=pfs, o=po,
-                                   workspace=ws)
-        else:
-            kda.kda_prefill_chunked(pq, pk, pv, pg, pbeta, ps0,
-                                    chunk_size=pp.C, final_state=pfs, o=po,
-                                    workspace=ws)
+            return
+        kda.kda_prefill_varlen_prep(pq_, pk_, pv_, pg_, pbeta_, cu, maxlen,
+                                    chunk_size=pp.C, workspace=ws)
+        if mid is not None:
+            mid.record(stream)
+        kda.kda_prefill_varlen_recur(ws, cu, maxlen, total, pp.H, pp.K, pp.V,
+                                     pq.dtype, ps0, chunk_size=pp.C,
+                                     final_state=pfs, o=po_)
 
     def decode(i):
         kda.kda_decode_step(dq, dk, dv, dg, dbeta, states[i % 3], o=do)
@@ -206,15 +215,15 @@ def main(argv=None):
 
     def step(i, rec=None):
         if rec is not None:
-            e0, e1, e2 = ev(), ev(), ev()
+            e0, em, e1, e2 = ev(), ev(), ev(), ev()
             e0.record(stream)
-        prefill()
+        prefill(None if rec is None or ck is not None else em)
         if rec is not None:
             e1.record(stream)
         decode(i)
         if rec is not None:
             e2.record(stream)
-            rec.append((e0, e1, e2))
+            rec.append((e0, None if ck is not None else em, e1, e2))
         if calib is not None:
             calib[1].copy_(calib[0])
 
@@ -230,8 +239,12 @@ def main(argv=None):
         step(i, rec)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_ms = [a.elapsed_time(b) for a, b, _ in rec]
-    dec_ms = [b.elapsed_time(c) for _, b, c in rec]
+    pre_ms = [a.elapsed_time(b) for a, _, b, _ in rec]
+    dec_ms = [b.elapsed_time(c) for _, _, b, c in rec]
+    prep_ms = recur_ms = None
+    if ck is None:
+        prep_ms = [a.elapsed_time(m) for a, m, _, _ in rec]
+        recur_ms = [m.elapsed_time(b) for _, m, b, _ in rec]
     ms_step = wall * 1e3 / args.steps
     pre_avg = float(np.mean(pre_ms))
     dec_avg = float(np.mean(dec_ms))
@@ -239,6 +252,9 @@ def main(argv=None):
     dec_med = float(np.median(dec_ms))
     log("timed %d steps: %.3f ms/step, prefill %.3f ms, decode %.4f ms"
         % (args.steps, ms_step, pre_avg, dec_avg))
+    if prep_ms is not None:
+        log("prefill stages: prep %.4f ms, recurrence %.4f ms"
+            % (float(np.mean(prep_ms)), float(np.mean(recur_ms))))
 
     # decode steps back to back (outside the timed region): the state traffic
     # of one step then overlaps the write-back of the previous one, the
@@ -294,7 +310,43 @@ def main(argv=None):
     pre_bytes_min = (counts.prefill_min_bytes_per_token_head(pp.K, pp.V) *
                      total * pp.H)
     pre_s = pre_avg * 1e-3
-    traffic = read_traffic("kda_decode.hip")
+    elt = pq.element_size()
+    prep_b = counts.prep_bytes(total * pp.H, chunks, pp.C, pp.K, pp.V, elt)
+    recur_b = counts.recur_bytes(total * pp.H, chunks, pp.C, pp.K, pp.V, elt)
+
+    def kernel_entry(name, src_file, nbytes, ms):
+        avg, med = float(np.mean(ms)), float(np.median(ms))
+        ach = nbytes / (avg * 1e-3) / 1e9
+        return {"kernel": name, "bound": "hbm", "achieved": round(ach, 2),
+                "peak": counts.HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(ach / counts.HBM_PEAK_GBPS, 4),
+                "traffic": read_traffic(src_file),
+                "algorithmic_bytes_per_launch": nbytes,
+                "avg_launch_ms": round(avg, 5),
+                "median_launch_ms": round(med, 5)}
+
+    kernels = []
+    if prep_ms is not None:
+        kernels.append(kernel_entry("prep_kernel (kda_prep.hip)",
+                                    "kda_prep.hip", prep_b, prep_ms))
+        kernels.append(kernel_entry("chunk recurrence (kda_recur.hip)",
+                                    "kda_recur.hip", recur_b, recur_ms))
+    dec_entry = kernel_entry("decode_kernel (kda_decode.hip)",
+                             "kda_decode.hip", dec_bytes, dec_ms)
+    dec_entry.update({
+        "copy_reference": copy_ref,
+        "vs_copy": None if copy_ref is None else
+            round(dec_gbps / copy_ref["achieved"], 4),
+        "back_to_back": None if b2b_ms is None else {
+            "launches": n_b2b,
+            "avg_launch_ms": round(b2b_ms, 5),
+            "achieved": round(dec_bytes / (b2b_ms * 1e-3) / 1e9, 2),
+            "frac": round(dec_bytes / (b2b_ms * 1e-3) / 1e9 /
+                          counts.HBM_PEAK_GBPS, 4),
+        }})
+    kernels.append(dec_entry)
+    # the roofline line is the kernel that takes the largest share of a step
+    dominant = max(kernels, key=lambda e: e["avg_launch_ms"])
 
     result = {
         "metric": METRIC,
@@ -323,28 +375,8 @@ def main(argv=None):
                                    else "nonzero"),
             "parallelism": "single GPU",
         },
-        "roofline": {
-            "kernel": "decode_kernel (kda_decode.hip)",
-            "bound": "hbm",
-            "achieved": round(dec_gbps, 2),
-            "peak": counts.HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(dec_gbps / counts.HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": dec_bytes,
-            "avg_launch_ms": round(dec_avg, 5),
-            "median_launch_ms": round(dec_med, 5),
-            "copy_reference": copy_ref,
-            "vs_copy": None if copy_ref is None else
-                round(dec_gbps / copy_ref["achieved"], 4),
-            "back_to_back": None if b2b_ms is None else {
-                "launches": n_b2b,
-                "avg_launch_ms": round(b2b_ms, 5),
-                "achieved": round(dec_bytes / (b2b_ms * 1e-3) / 1e9, 2),
-                "frac": round(dec_bytes / (b2b_ms * 1e-3) / 1e9 /
-                              counts.HBM_PEAK_GBPS, 4),
-            },
-        },
+        "roofline": dominant,
+        "kernels": kernels,
         "prefill": {
             "tokens_per_s": round(total / pre_s, 1),
             "ms": round(pre_avg, 4),
@@ -357,7 +389,7 @@ def main(argv=None):
             "mfma_util_frac": round(pre_flops / pre_s / 1e12 /
                                     counts.BF16_MFMA_PEAK_TFLOPS, 4),
             "roofline": {
-                "kernels": "prep_kernel + recurrence kernel (one library call)",
+                "kernels": "prep_kernel + recurrence kernel",
                 "bound": "hbm",
                 "achieved": round(pre_bytes_pages / pre_s / 1e9, 2),
                 "peak": counts.HBM_PEAK_GBPS,

@@ -143,6 +143,38 @@ kda_status_t kda_prefill_varlen(const void* q, const void* k, const void* v,
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * The two stages of kda_prefill_varlen, for callers that schedule them
+ * separately or time them apart ("Kimi K3: The Manos, The Mythos, The
+ * Legendos", section "FlashKDA algorithm": the first kernel prepares every
+ * chunk's tensors independently, the second carries the state across the
+ * chunks).  kda_prefill_varlen_prep reads q, k, v, g, beta and cu_seqlens and
+ * writes only the workspace.  kda_prefill_varlen_recur reads the workspace,
+ * cu_seqlens and initial_state and writes o and final_state.  Its workspace
+ * must hold what kda_prefill_varlen_prep wrote for the same cu_seqlens, N,
+ * total_T, max_seqlen, H, Dk, Dv, C and dtype, and must not be changed in
+ * between.  Called in that order on one stream, the pair computes what
+ * kda_prefill_varlen computes, bit for bit.
+ * Arguments, layouts and errors as kda_prefill_varlen; the prep stage does
+ * not take o or the states, the recurrence stage not q, k, v, g, beta.
+ */
+kda_status_t kda_prefill_varlen_prep(const void* q, const void* k,
+                                     const void* v, const float* g,
+                                     const float* beta,
+                                     const int32_t* cu_seqlens, int32_t N,
+                                     int64_t total_T, int32_t max_seqlen,
+                                     int32_t H, int32_t Dk, int32_t Dv,
+                                     int32_t C, int32_t dtype, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+kda_status_t kda_prefill_varlen_recur(const int32_t* cu_seqlens, int32_t N,
+                                      int64_t total_T, int32_t max_seqlen,
+                                      const float* initial_state,
+                                      float* final_state, void* o, int32_t H,
+                                      int32_t Dk, int32_t Dv, int32_t C,
+                                      float scale, int32_t dtype,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
  * kda_prefill_varlen that also stores the recurrent state at a fixed token
  * interval inside every sequence ("Kimi K3: The Manos, The Mythos, The
  * Legendos", section "KDA prefix cache management": since the longest shared

@@ -57,3 +57,21 @@ def recur_bytes_per_chunk(C: int, K: int, V: int, out_bytes: int = 2) -> int:
     """Chunk-recurrence kernel, one full chunk and head: reads W, Q^, K-bar,
     U~, M and gamma once; writes o."""
     return 3 * C * K * 2 + C * V * 2 + C * C * 2 + K * 4 + C * V * out_bytes
+
+
+def prep_bytes(token_heads: int, chunk_heads: int, C: int, K: int, V: int,
+               in_bytes: int = 2) -> int:
+    """Chunk-prep kernel over a whole call: every (token, head) row of q, k,
+    v, g and beta read once; every (chunk, head) writes its full blocks (a
+    partial chunk's padding rows included), as in prep_bytes_per_chunk."""
+    reads = token_heads * ((2 * K + V) * in_bytes + K * 4 + 4)
+    writes = chunk_heads * (3 * C * K * 2 + C * V * 2 + C * C * 2 + K * 4)
+    return reads + writes
+
+
+def recur_bytes(token_heads: int, chunk_heads: int, C: int, K: int, V: int,
+                out_bytes: int = 2) -> int:
+    """Chunk-recurrence kernel over a whole call: every (chunk, head) block
+    of the workspace read once, every (token, head) row of o written once."""
+    return (chunk_heads * (3 * C * K * 2 + C * V * 2 + C * C * 2 + K * 4) +
+            token_heads * V * out_bytes)

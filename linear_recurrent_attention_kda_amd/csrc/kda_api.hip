@@ -32,9 +32,14 @@ kda_status_t check_prefill_common(int32_t H, int32_t Dk, int32_t Dv,
   return KDA_OK;
 }
 
+// Stages of a prefill call: the chunk-prep kernel (writes the workspace) and
+// the chunk-recurrence kernel (reads it).
+constexpr int kStagePrep = 1, kStageRecur = 2, kStagesBoth = 3;
+
 kda_status_t run_prefill(kda::PrefillArgs& a, int32_t D, int32_t C,
                          int32_t dtype, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         size_t workspace_bytes, void* stream,
+                         int stages = kStagesBoth) {
   const size_t need = kda_prefill_workspace_size(a.N, a.total_T, a.H, D, D, C);
   if (need == 0) return KDA_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
@@ -46,11 +51,12 @@ kda_status_t run_prefill(kda::PrefillArgs& a, int32_t D, int32_t C,
   a.nslots = kda::num_slots(a.N, a.total_T, C);
   const bool bf16_io = dtype == KDA_DTYPE_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (a.total_T > 0 && a.max_chunks > 0) {
+  if ((stages & kStagePrep) && a.total_T > 0 && a.max_chunks > 0) {
     if (kda::launch_prep(a, D, C, bf16_io, st) != hipSuccess)
       return KDA_ERR_LAUNCH;
   }
-  if (kda::launch_recur(a, D, C, bf16_io, st) != hipSuccess)
+  if ((stages & kStageRecur) &&
+      kda::launch_recur(a, D, C, bf16_io, st) != hipSuccess)
     return KDA_ERR_LAUNCH;
   return KDA_OK;
 }
@@ -78,14 +84,22 @@ kda_status_t prefill_varlen(const void* q, const void* k, const void* v,
                             bool want_ckpt, int32_t ckpt_every,
                             float* ckpt_states, size_t ckpt_bytes,
                             const float* conv_w, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            size_t workspace_bytes, void* stream,
+                            int stages = kStagesBoth) {
   if (N <= 0 || total_T < 0 || max_seqlen < 0) return KDA_ERR_INVALID_ARG;
   if (total_T > 0 && max_seqlen == 0) return KDA_ERR_INVALID_ARG;
   kda_status_t st = check_prefill_common(H, Dk, Dv, C, dtype);
   if (st != KDA_OK) return st;
   if (N > 65535) return KDA_ERR_UNSUPPORTED;
   if (!cu_seqlens || !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARG;
-  st = check_tensors(total_T, q, k, v, g, beta, o);
+  if (stages == kStagesBoth) {
+    st = check_tensors(total_T, q, k, v, g, beta, o);
+  } else if (stages == kStagePrep) {
+    // the inputs only (o is not touched)
+    st = check_tensors(total_T, q, k, v, g, beta, q);
+  } else if (total_T > 0 && (!o || !aligned(o, 16))) {
+    st = KDA_ERR_INVALID_ARG;  // the recurrence: o only
+  }
   if (st != KDA_OK) return st;
   if ((initial_state && !aligned(initial_state, 16)) ||
       (final_state && !aligned(final_state, 16)))
@@ -119,7 +133,8 @@ kda_status_t prefill_varlen(const void* q, const void* k, const void* v,
   a.ckpt_states =
       (want_ckpt && total_T / ckpt_every > 0) ? ckpt_states : nullptr;
   a.conv_w = conv_w;
-  return run_prefill(a, Dk, C, dtype, workspace, workspace_bytes, stream);
+  return run_prefill(a, Dk, C, dtype, workspace, workspace_bytes, stream,
+                     stages);
 }
 
 kda_status_t decode_step(const void* q, const void* k, const void* v,
@@ -228,6 +243,35 @@ kda_status_t kda_prefill_varlen(const void* q, const void* k, const void* v,
                         initial_state, final_state, o, H, Dk, Dv, C, scale,
                         dtype, false, 0, nullptr, 0, nullptr, workspace,
                         workspace_bytes, stream);
+}
+
+kda_status_t kda_prefill_varlen_prep(const void* q, const void* k,
+                                     const void* v, const float* g,
+                                     const float* beta,
+                                     const int32_t* cu_seqlens, int32_t N,
+                                     int64_t total_T, int32_t max_seqlen,
+                                     int32_t H, int32_t Dk, int32_t Dv,
+                                     int32_t C, int32_t dtype, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return prefill_varlen(q, k, v, g, beta, cu_seqlens, N, total_T, max_seqlen,
+                        nullptr, nullptr, nullptr, H, Dk, Dv, C, 1.0f, dtype,
+                        false, 0, nullptr, 0, nullptr, workspace,
+                        workspace_bytes, stream, kStagePrep);
+}
+
+kda_status_t kda_prefill_varlen_recur(const int32_t* cu_seqlens, int32_t N,
+                                      int64_t total_T, int32_t max_seqlen,
+                                      const float* initial_state,
+                                      float* final_state, void* o, int32_t H,
+                                      int32_t Dk, int32_t Dv, int32_t C,
+                                      float scale, int32_t dtype,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  return prefill_varlen(nullptr, nullptr, nullptr, nullptr, nullptr,
+                        cu_seqlens, N, total_T, max_seqlen, initial_state,
+                        final_state, o, H, Dk, Dv, C, scale, dtype, false, 0,
+                        nullptr, 0, nullptr, workspace, workspace_bytes,
+                        stream, kStageRecur);
 }
 
 kda_status_t kda_prefill_varlen_ckpt(

@@ -63,6 +63,14 @@ def load() -> ctypes.CDLL:
         lib.kda_prefill_varlen.argtypes = [
             vp, vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, i32,
             i32, f32, i32, vp, sz, vp]
+        lib.kda_prefill_varlen_prep.restype = i32
+        lib.kda_prefill_varlen_prep.argtypes = [
+            vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, i32,
+            vp, sz, vp]
+        lib.kda_prefill_varlen_recur.restype = i32
+        lib.kda_prefill_varlen_recur.argtypes = [
+            vp, i32, i64, i32, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp,
+            sz, vp]
         lib.kda_prefill_varlen_ckpt.restype = i32
         lib.kda_prefill_varlen_ckpt.argtypes = [
             vp, vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, i32,
@@ -235,6 +243,67 @@ def kda_prefill_varlen(q, k, v, g, beta, cu_seqlens, max_seqlen: int,
         _ptr(workspace), workspace.numel(), _stream(dev))
     if st != KDA_OK:
         raise KDAError("kda_prefill_varlen", st)
+    return o, final_state
+
+
+def kda_prefill_varlen_prep(q, k, v, g, beta, cu_seqlens, max_seqlen: int,
+                            *, chunk_size: int = 64, workspace=None):
+    """First stage of kda_prefill_varlen: every chunk's tensors, written to
+    the workspace (allocated when None).  Returns the workspace, to be passed
+    unchanged to kda_prefill_varlen_recur."""
+    lib = load()
+    total_T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    N = cu_seqlens.numel() - 1
+    for t, n, s, dt in ((q, "q", (total_T, H, Dk), q.dtype),
+                        (k, "k", (total_T, H, Dk), q.dtype),
+                        (v, "v", (total_T, H, Dv), q.dtype),
+                        (g, "g", (total_T, H, Dk), torch.float32),
+                        (beta, "beta", (total_T, H), torch.float32),
+                        (cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)):
+        _check(t, n, s, dt, dev)
+    if workspace is None:
+        workspace = workspace_for(N, total_T, H, Dk, Dv, chunk_size, dev)
+    st = lib.kda_prefill_varlen_prep(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N,
+        total_T, int(max_seqlen), H, Dk, Dv, chunk_size, _dtype_code(q),
+        _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_prefill_varlen_prep", st)
+    return workspace
+
+
+def kda_prefill_varlen_recur(workspace, cu_seqlens, max_seqlen: int,
+                             total_T: int, H: int, Dk: int, Dv: int,
+                             dtype, initial_state=None, *,
+                             chunk_size: int = 64, scale: float = 1.0,
+                             output_final_state: bool = True,
+                             final_state=None, o=None):
+    """Second stage of kda_prefill_varlen: the recurrence over the chunks
+    that kda_prefill_varlen_prep wrote to `workspace`.  dtype is the torch
+    dtype of q, k, v (and of o).  Returns (o, final_state or None)."""
+    lib = load()
+    dev = workspace.device
+    N = cu_seqlens.numel() - 1
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (N, H, Dk, Dv), torch.float32,
+               dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32,
+                                  device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (N, H, Dk, Dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((total_T, H, Dv), dtype=dtype, device=dev)
+    _check(o, "o", (total_T, H, Dv), dtype, dev)
+    st = lib.kda_prefill_varlen_recur(
+        _ptr(cu_seqlens), N, total_T, int(max_seqlen), _ptr(initial_state),
+        _ptr(final_state), _ptr(o), H, Dk, Dv, chunk_size, scale,
+        _dtype_code(o), _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_prefill_varlen_recur", st)
     return o, final_state
 
 

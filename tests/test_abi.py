@@ -27,7 +27,9 @@ def test_exports_every_declared_symbol():
                           "kda_decode_step", "kda_spec_verify",
                           "kda_spec_commit", "kda_output_norm_gate",
                           "kda_decode_step_gated",
-                          "kda_prefill_varlen_prologue"}
+                          "kda_prefill_varlen_prologue",
+                          "kda_prefill_varlen_prep",
+                          "kda_prefill_varlen_recur"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -126,6 +128,50 @@ def test_prefill_varlen_validation():
     assert _varlen(lib, C=8) == UNSUP
     assert _varlen(lib, ws_bytes=10) == WS
     assert _varlen(lib, v=NULL) == INVALID
+
+
+def _prep(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, cu=P, N=2, total=300, maxlen=200,
+             H=2, Dk=64, Dv=64, C=32, dtype=0, ws=P, ws_bytes=1 << 40,
+             stream=NULL)
+    a.update(kw)
+    return lib.kda_prefill_varlen_prep(
+        a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"],
+        a["total"], a["maxlen"], a["H"], a["Dk"], a["Dv"], a["C"],
+        a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _recur(lib, **kw):
+    a = dict(cu=P, N=2, total=300, maxlen=200, s0=NULL, s1=NULL, o=P, H=2,
+             Dk=64, Dv=64, C=32, scale=1.0, dtype=0, ws=P, ws_bytes=1 << 40,
+             stream=NULL)
+    a.update(kw)
+    return lib.kda_prefill_varlen_recur(
+        a["cu"], a["N"], a["total"], a["maxlen"], a["s0"], a["s1"], a["o"],
+        a["H"], a["Dk"], a["Dv"], a["C"], a["scale"], a["dtype"], a["ws"],
+        a["ws_bytes"], a["stream"])
+
+
+def test_prefill_stage_validation():
+    """The two stages check what they read and write; every call here fails
+    validation (nothing is launched)."""
+    lib = kda.load()
+    assert _prep(lib, N=0) == INVALID
+    assert _prep(lib, cu=NULL) == INVALID
+    assert _prep(lib, maxlen=0) == INVALID
+    assert _prep(lib, q=NULL) == INVALID
+    assert _prep(lib, g=MIS) == INVALID
+    assert _prep(lib, C=8) == UNSUP
+    assert _prep(lib, dtype=5) == UNSUP
+    assert _prep(lib, ws_bytes=10) == WS
+    assert _prep(lib, ws=NULL) == WS
+    assert _recur(lib, N=0) == INVALID
+    assert _recur(lib, cu=NULL) == INVALID
+    assert _recur(lib, o=NULL) == INVALID
+    assert _recur(lib, o=MIS) == INVALID
+    assert _recur(lib, s0=MIS) == INVALID
+    assert _recur(lib, Dk=48, Dv=48) == UNSUP
+    assert _recur(lib, ws_bytes=10) == WS
 
 
 def _ckpt(lib, **kw):
