@@ -17,7 +17,10 @@ namespace kda {
 //   W    fragments (m, kk)  : rows of (I + A)^-1 diag(beta) Khat       [C x Dk]
 //   Qh   fragments (m, kk)  : q * exp(a)                              [C x Dk]
 //   KbT  fragments (ct, cs) : (k * exp(a_last - a))^T                 [Dk x C]
-//   M    fragments (m, cs)  : decayed Q K^T, lower incl. diag, 0 above [C x C]
+//   M    fragments (m, cs)  : decayed Q K^T, lower incl. diag, 0 above [C x C];
+//                             only fragments with 2 cs <= m are written (the
+//                             others are entirely above the diagonal, zero,
+//                             and never read)
 //   UtT  fragments (jt, m)  : ((I + A)^-1 diag(beta) v)^T, 8 bytes per lane
 //                             (row j = 16jt + l%16, cols 16m + 4(l/16)..+3)
 //   gamma[Dk] fp32          : exp(a_last)

@@ -545,9 +545,14 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a) {
         ++m;
       }
       const int nn = m + 1 + z;
-      *reinterpret_cast<uint2*>(
-          gM + WsLayout::frag16(16 * m + rl, 16 * nn + 4 * kg, lay.cst)) =
-          make_uint2(0u, 0u);
+      // only inside 32-column groups that the recurrence reads: group cs of
+      // row tile m is read when 2 cs <= m (it holds a tile at or below the
+      // diagonal); the groups further right are entirely zero and are
+      // neither written nor read
+      if (2 * (nn / 2) <= m)
+        *reinterpret_cast<uint2*>(
+            gM + WsLayout::frag16(16 * m + rl, 16 * nn + 4 * kg, lay.cst)) =
+            make_uint2(0u, 0u);
     }
   }
   __syncthreads();  // A complete; the row operands and column base are dead

@@ -182,7 +182,13 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
       for (int cs = 0; cs < CSTEPS; ++cs) {
         const int s0 = 32 * cs + 8 * kg;   // M is zero above the diagonal
         if (kFullC || s0 < C)
-          op.m[cs] = load_bf16x8(b.M + ((mrow * lay.cst + cs) * 64 + lane) * 8);
+        {
+          // fragments right of the diagonal's are never written (zero): the
+          // load stays branch-free and its value is replaced by zero
+          const bf16x8 mv =
+              load_bf16x8(b.M + ((mrow * lay.cst + cs) * 64 + lane) * 8);
+          op.m[cs] = 2 * cs <= mrow ? mv : zero_bf16x8();
+        }
       }
     }
   };
@@ -492,8 +498,9 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
       for (int f = 0; f < KT * CSTEPS; ++f)
         copy1k(blk + lay.off_KbT + 1024 * f, base + OB::KB + 1024 * f);
 #pragma unroll
-      for (int f = 0; f < MT * CSTEPS; ++f)
-        copy1k(blk + lay.off_M + 1024 * f, base + OB::M + 1024 * f);
+      for (int f = 0; f < MT * CSTEPS; ++f)  // fragments (m, cs), 2 cs <= m
+        if (2 * (f % CSTEPS) <= f / CSTEPS)
+          copy1k(blk + lay.off_M + 1024 * f, base + OB::M + 1024 * f);
 #pragma unroll
       for (int f = 0; f < D / 64; ++f)  // gamma: 256 B per instruction
         copy4_to_lds(blk + lay.off_gamma + 256 * f + 4 * lane,
@@ -596,8 +603,10 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
     float4 gm[NCT];
 #pragma unroll
     for (int cs = 0; cs < CSTEPS; ++cs) {
-      mf[cs] = *reinterpret_cast<const bf16x8*>(
-          ob + OB::M + ((mrow * CSTEPS + cs) * 64 + lane) * 16);
+      mf[cs] = zero_bf16x8();
+      if (2 * cs <= mrow)  // the others were not copied (zero)
+        mf[cs] = *reinterpret_cast<const bf16x8*>(
+            ob + OB::M + ((mrow * CSTEPS + cs) * 64 + lane) * 16);
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt)
         ubf[jt][cs] = *reinterpret_cast<const bf16x8*>(
@@ -620,7 +629,7 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
       const int jt = (u0 + i) % JT;
 #pragma unroll
       for (int cs = 0; cs < CSTEPS; ++cs)
-        Ot[i] = mfma_bf16(ubf[jt][cs], mf[cs], Ot[i]);
+        if (2 * cs <= mrow) Ot[i] = mfma_bf16(ubf[jt][cs], mf[cs], Ot[i]);
       const int r = 16 * mrow + rl;
       buffer_store4(o, orsrc,
                     (uint32_t)(((int64_t)r * H * V + 16 * jt + 4 * kg) *
