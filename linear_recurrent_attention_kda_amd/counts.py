@@ -44,28 +44,24 @@ def prefill_min_bytes_per_token_head(K: int, V: int, in_bytes: int = 2) -> int:
     return (2 * K + 2 * V) * in_bytes + 4 * K + 4
 
 
-def prep_bytes_per_chunk(C: int, K: int, V: int, in_bytes: int = 2) -> int:
-    """Chunk-prep kernel, one full chunk and head: reads q, k, v, g, beta;
-    writes W, Q^, K-bar (C x K bf16), U~ (C x V bf16), M (C x C bf16) and
-    gamma (K fp32)."""
-    reads = C * (2 * K + V) * in_bytes + C * K * 4 + C * 4
-    writes = 3 * C * K * 2 + C * V * 2 + C * C * 2 + K * 4
-    return reads + writes
-
-
-def recur_bytes_per_chunk(C: int, K: int, V: int, out_bytes: int = 2) -> int:
-    """Chunk-recurrence kernel, one full chunk and head: reads W, Q^, K-bar,
-    U~, M and gamma once; writes o."""
-    return 3 * C * K * 2 + C * V * 2 + C * C * 2 + K * 4 + C * V * out_bytes
+def m_block_bytes(C: int) -> int:
+    """Bytes of the decayed Q K^T block M that the kernels move per chunk and
+    head: its 16 x 32 bf16 fragments (m, cs) with 2 cs <= m, those that hold
+    a tile at or below the diagonal (the others are zero and never moved)."""
+    mt, cst = C // 16, (C + 31) // 32
+    frags = sum(min(m // 2 + 1, cst) for m in range(mt))
+    return frags * 16 * 32 * 2
 
 
 def prep_bytes(token_heads: int, chunk_heads: int, C: int, K: int, V: int,
                in_bytes: int = 2) -> int:
     """Chunk-prep kernel over a whole call: every (token, head) row of q, k,
     v, g and beta read once; every (chunk, head) writes its full blocks (a
-    partial chunk's padding rows included), as in prep_bytes_per_chunk."""
+    partial chunk's padding rows included) and M's fragments at or below
+    the diagonal."""
     reads = token_heads * ((2 * K + V) * in_bytes + K * 4 + 4)
-    writes = chunk_heads * (3 * C * K * 2 + C * V * 2 + C * C * 2 + K * 4)
+    writes = chunk_heads * (3 * C * K * 2 + C * V * 2 + m_block_bytes(C) +
+                            K * 4)
     return reads + writes
 
 
@@ -73,5 +69,6 @@ def recur_bytes(token_heads: int, chunk_heads: int, C: int, K: int, V: int,
                 out_bytes: int = 2) -> int:
     """Chunk-recurrence kernel over a whole call: every (chunk, head) block
     of the workspace read once, every (token, head) row of o written once."""
-    return (chunk_heads * (3 * C * K * 2 + C * V * 2 + C * C * 2 + K * 4) +
+    return (chunk_heads * (3 * C * K * 2 + C * V * 2 + m_block_bytes(C) +
+                           K * 4) +
             token_heads * V * out_bytes)
