@@ -182,13 +182,9 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
       for (int cs = 0; cs < CSTEPS; ++cs) {
         const int s0 = 32 * cs + 8 * kg;   // M is zero above the diagonal
         if (kFullC || s0 < C)
-        {
-          // fragments right of the diagonal's are never written (zero): the
-          // load stays branch-free and its value is replaced by zero
-          const bf16x8 mv =
-              load_bf16x8(b.M + ((mrow * lay.cst + cs) * 64 + lane) * 8);
-          op.m[cs] = 2 * cs <= mrow ? mv : zero_bf16x8();
-        }
+          // (fragments with 2 cs > mrow are never written, and the product
+          // below skips them; the load stays branch-free)
+          op.m[cs] = load_bf16x8(b.M + ((mrow * lay.cst + cs) * 64 + lane) * 8);
       }
     }
   };
@@ -287,7 +283,8 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
         const int jt = (u0 + i) % JT;
 #pragma unroll
         for (int cs = 0; cs < CSTEPS; ++cs)
-          Ot[i] = mfma_bf16(ubf[jt][cs], op.m[cs], Ot[i]);
+          if (2 * cs <= mrow)  // M is zero right of that
+            Ot[i] = mfma_bf16(ubf[jt][cs], op.m[cs], Ot[i]);
         const int r = 16 * mrow + rl;
         buffer_store4(o, orsrc,
                       (uint32_t)(((int64_t)r * H * V + 16 * jt + 4 * kg) *
