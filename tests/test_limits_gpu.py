@@ -70,3 +70,43 @@ def test_longest_speculative_draft():
     es = U.slice_rel(U.host(state), s_ref, (0, 1))
     U.log("spec T=16: o %.3e state %.3e" % (eo, es))
     assert eo <= U.DECODE_O_TOL["bf16"] and es <= U.DECODE_STATE_TOL
+
+
+def test_inputs_beyond_4_gib():
+    """147,456 tokens x 64 heads at d = 128: g is 4.8 GB of fp32 and q, k,
+    v and o 2.4 GB of bf16 each, so the last chunks sit at byte offsets
+    past 2^32 (and the workspace holds 11 GB).  Only a 9,216-token x 8-head
+    block is drawn; the device repeats it 16 times along the tokens and 8
+    times along the heads.  Heads with equal inputs must give equal outputs
+    and states bit for bit, and heads 0 and 63 (a repeat of head 7) must
+    match the oracle run on the same repeated values."""
+    base = inputs.make("prefill", seed=55, B=1, T=9216, H=8, s0=True)
+    rt, rh = 16, 8
+    T, H = base.T * rt, base.H * rh
+    U.log("prefill beyond 4 GiB: T=%d H=%d" % (T, H))
+
+    def tiled(x, dtype):
+        t = U.to_dev(x, dtype)
+        return t.repeat((1, rt, rh) + (1,) * (t.dim() - 3))
+
+    q, k, v = (tiled(x, base.dtype) for x in (base.q, base.k, base.v))
+    g, beta = tiled(base.g, "fp32"), tiled(base.beta, "fp32")
+    s0 = U.f32_dev(base.initial_state).repeat(1, rh, 1, 1)
+    assert g.numel() * 4 > 4 * 2 ** 30
+    o, s = kda.kda_prefill_chunked(q, k, v, g, beta, s0, chunk_size=base.C)
+    torch.cuda.synchronize()
+    del q, k, v, g, beta
+    h0 = base.H
+    for j in range(1, rh):
+        assert torch.equal(o[:, :, :h0], o[:, :, j * h0:(j + 1) * h0]), j
+        assert torch.equal(s[:, :h0], s[:, j * h0:(j + 1) * h0]), j
+    for dev_head, h in ((0, 0), (H - 1, h0 - 1)):
+        rep = lambda x: np.tile(x[:, :, [h]], (1, rt, 1, 1))  # noqa: E731
+        o_ref, s_ref = oracle.run_fixed(
+            rep(base.q), rep(base.k), rep(base.v), rep(base.g),
+            np.tile(base.beta[:, :, [h]], (1, rt, 1)),
+            base.initial_state[:, [h]])
+        eo = U.prefill_o_rel(U.host(o[:, :, [dev_head]]), o_ref)
+        es = U.slice_rel(U.host(s[:, [dev_head]]), s_ref, (0, 1))
+        U.log("   head %d: o rel %.3e state rel %.3e" % (dev_head, eo, es))
+        assert eo <= U.PREFILL_TOL and es <= U.PREFILL_TOL
