@@ -57,12 +57,13 @@ def source_hash(name: str) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel_file: str):
-    """HBM bytes per launch measured with rocprofv3 counters for the current
-    source of `kernel_file` (profiles/traffic_<name>.txt), or None when no
-    measurement exists or the kernel changed since it was taken."""
-    path = os.path.join(PROFILES, "traffic_%s.txt" %
-                        kernel_file.replace(".hip", ""))
+def read_counters(kind: str, kernel_file: str):
+    """Per-launch rocprofv3 counter figures stored in
+    profiles/<kind>_<name>.txt (key = value lines), as floats, or None when
+    no measurement exists or the kernel's source changed since it was
+    taken."""
+    path = os.path.join(PROFILES, "%s_%s.txt" %
+                        (kind, kernel_file.replace(".hip", "")))
     if not os.path.exists(path):
         return None
     kv = {}
@@ -70,12 +71,41 @@ def read_traffic(kernel_file: str):
         if "=" in line and not line.startswith("#"):
             key, val = line.split("=", 1)
             kv[key.strip()] = val.strip()
-    if kv.get("source_sha256_16") != source_hash(kernel_file):
+    if kv.pop("source_sha256_16", None) != source_hash(kernel_file):
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
+        return {key: float(val) for key, val in kv.items()}
+    except ValueError:
         return None
+
+
+def read_traffic(kernel_file: str):
+    """HBM bytes per launch measured with FETCH_SIZE / WRITE_SIZE for the
+    current source of `kernel_file`, or None."""
+    kv = read_counters("traffic", kernel_file)
+    return None if kv is None else kv.get("hbm_bytes_per_launch")
+
+
+def mfma_figures(kernel_file: str, avg_ms: float):
+    """Matrix-core work of one launch from the stored MFMA counters
+    (SQ_INSTS_VALU_MFMA_MOPS_* count 512 FLOPs each; SQ_VALU_MFMA_BUSY_CYCLES
+    sums over SIMDs), over the live average launch time: achieved TFLOP/s
+    against the bf16 peak, and the share of SIMD cycles the matrix cores
+    were busy.  None without a measurement for the current source."""
+    kv = read_counters("mfma", kernel_file)
+    if kv is None:
+        return None
+    bf16 = kv["bf16_mops"] * 512
+    f32 = kv["f32_mops"] * 512
+    s = avg_ms * 1e-3
+    return {"bf16_flop_per_launch": int(bf16),
+            "f32_flop_per_launch": int(f32),
+            "achieved_tflops": round((bf16 + f32) / s / 1e12, 2),
+            "peak_tflops": counts.BF16_MFMA_PEAK_TFLOPS,
+            "frac": round(bf16 / s / 1e12 / counts.BF16_MFMA_PEAK_TFLOPS +
+                          f32 / s / 1e12 / counts.FP32_MFMA_PEAK_TFLOPS, 4),
+            "busy_frac": round(kv["busy_cycles"] /
+                               (s * counts.CLOCK_HZ * counts.SIMDS), 4)}
 
 
 def cpu_model() -> str:
@@ -323,7 +353,8 @@ def main(argv=None):
                 "traffic": read_traffic(src_file),
                 "algorithmic_bytes_per_launch": nbytes,
                 "avg_launch_ms": round(avg, 5),
-                "median_launch_ms": round(med, 5)}
+                "median_launch_ms": round(med, 5),
+                "mfma": mfma_figures(src_file, avg)}
 
     kernels = []
     if prep_ms is not None:

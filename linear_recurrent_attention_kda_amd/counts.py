@@ -10,6 +10,9 @@ from __future__ import annotations
 HBM_PEAK_GBPS = 8000.0            # HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0    # dense bf16 matrix cores, TFLOP/s
 FP32_VECTOR_PEAK_TFLOPS = 157.3
+FP32_MFMA_PEAK_TFLOPS = 157.3     # dense fp32 matrix cores, TFLOP/s
+SIMDS = 256 * 4                   # 256 compute units of 4 SIMDs
+CLOCK_HZ = 2.4e9                  # peak engine clock
 
 
 def decode_flops_per_head(D: int) -> int:

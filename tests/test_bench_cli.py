@@ -27,3 +27,31 @@ def test_decode_byte_count_of_the_workload():
     from linear_recurrent_attention_kda_amd import counts
     # 64 sequences x 96 heads, d = 128: the fp32 state read and written once
     assert counts.decode_bytes_per_head(128) * 64 * 96 == 805_306_368
+
+
+def _stored(kind, name):
+    kv = {}
+    for line in open(os.path.join(ROOT, "profiles", "%s_%s.txt" % (kind, name))):
+        if "=" in line and not line.startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    return kv
+
+
+def test_stored_mfma_counts_equal_the_kernels_products():
+    """The matrix-core FLOPs rocprofv3 counted per launch (512 per MOPS unit)
+    equal a count of the products each kernel issues, on the 8192-token,
+    96-head prefill (C = 64, d = 128: 128 chunks x 96 heads)."""
+    C, D, units = 64, 128, 128 * 96
+    # prep: A and M over the 10 sub-tile pairs n <= m (16 x 16 x D each);
+    # W and U~ per 16-row tile m over k-extents 32, 32, 64, 64 (16 (m + 1)
+    # rounded up to the 32-deep bf16 MFMA step)
+    prep = 10 * 2 * (16 * 16 * D * 2) + 2 * (16 * D * 2) * (32 + 32 + 64 + 64)
+    # recurrence: W S, Q^ S and K^T U (2 C D^2 each) and M U over the six
+    # of M's eight 16 x 32 fragments that are not all zero
+    recur = 3 * 2 * C * D * D + 2 * C * C * D * 6 // 8
+    assert float(_stored("mfma", "kda_prep")["bf16_mops"]) * 512 == \
+        prep * units
+    assert float(_stored("mfma", "kda_recur")["bf16_mops"]) * 512 == \
+        recur * units
+    assert float(_stored("mfma", "kda_decode")["bf16_mops"]) == 0.0
