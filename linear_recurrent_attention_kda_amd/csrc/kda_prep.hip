@@ -258,12 +258,39 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a) {
     const __amdgpu_buffer_rsrc_t Wv = make_rsrc(
         static_cast<const Tin*>(a.v) + wrow0 * V,
         (uint32_t)((wspan * V + V) * sizeof(Tin)));
+    // Issue order: the head's taps (small, shared by all of the head's
+    // chunks), then a and b, then the convolution windows.  Loads complete
+    // in order, so storing the taps to LDS waits for the taps only, and the
+    // gates wait for a and b only, while the windows are still arriving.
     // taps of this head: [3][D][4] fp32, staged in LDS
+    constexpr int NTAP = 3 * D * kConvTaps;
+    constexpr int TPT = (NTAP + NT - 1) / NT;  // taps per thread
     const float* taps = a.conv_w + (size_t)h * D * kConvTaps;
-    for (int e = tid; e < 3 * D * kConvTaps; e += NT) {
+    float tapv[TPT];
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int e = tid + u * NT;
       const int x = e / (D * kConvTaps), rem = e % (D * kConvTaps);
-      s_taps[x][rem / kConvTaps][rem % kConvTaps] =
-          taps[(size_t)x * H * D * kConvTaps + rem];
+      tapv[u] = (NTAP % NT == 0 || e < NTAP)
+                    ? taps[(size_t)x * H * D * kConvTaps + rem] : 0.f;
+    }
+    float av[RPT][8];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const uint32_t row = (uint32_t)((r0 + i) * H);
+      if (active) {
+        const uint4 g0 = buffer_load_16(Rg, (row * K + c0) * 4);
+        const uint4 g1 = buffer_load_16(Rg, (row * K + c0 + 4) * 4);
+        av[i][0] = __uint_as_float(g0.x); av[i][1] = __uint_as_float(g0.y);
+        av[i][2] = __uint_as_float(g0.z); av[i][3] = __uint_as_float(g0.w);
+        av[i][4] = __uint_as_float(g1.x); av[i][5] = __uint_as_float(g1.y);
+        av[i][6] = __uint_as_float(g1.z); av[i][7] = __uint_as_float(g1.w);
+        bt[i] = buffer_load_f32(Rb, row * 4);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av[i][e] = 0.f;
+        bt[i] = 0.f;
+      }
     }
     Raw8<Tin> wq[NWIN], wk[NWIN], wv[NWIN];
     // window row j of this thread is packed row t0 + r0 - 3 + j; its offset
@@ -283,27 +310,20 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const uint32_t row = (uint32_t)((r0 + i) * H);
-      float av[8];
-      if (active) {
-        const uint4 g0 = buffer_load_16(Rg, (row * K + c0) * 4);
-        const uint4 g1 = buffer_load_16(Rg, (row * K + c0 + 4) * 4);
-        av[0] = __uint_as_float(g0.x); av[1] = __uint_as_float(g0.y);
-        av[2] = __uint_as_float(g0.z); av[3] = __uint_as_float(g0.w);
-        av[4] = __uint_as_float(g1.x); av[5] = __uint_as_float(g1.y);
-        av[6] = __uint_as_float(g1.z); av[7] = __uint_as_float(g1.w);
-        bt[i] = buffer_load_f32(Rb, row * 4);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) av[e] = 0.f;
-        bt[i] = 0.f;
+    for (int u = 0; u < TPT; ++u) {
+      const int e = tid + u * NT;
+      if (NTAP % NT == 0 || e < NTAP) {
+        const int x = e / (D * kConvTaps), rem = e % (D * kConvTaps);
+        s_taps[x][rem / kConvTaps][rem % kConvTaps] = tapv[u];
       }
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
       // rows past L must keep g = 0 and beta = 0 (no decay, no write)
       const bool live = r0 + i < it.L;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        gx[i][e] = live ? -5.f / (1.f + __builtin_amdgcn_exp2f(-av[e] * kLog2e))
+        gx[i][e] = live ? -5.f / (1.f + __builtin_amdgcn_exp2f(-av[i][e] * kLog2e))
                         : 0.f;
       bt[i] = live ? 1.f / (1.f + __builtin_amdgcn_exp2f(-bt[i] * kLog2e))
                    : 0.f;
