@@ -317,16 +317,22 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a) {
         s_taps[x][rem / kConvTaps][rem % kConvTaps] = tapv[u];
       }
     }
+    // sigmoid(x) = 1 / (1 + 2^(-x log2 e)) with the hardware reciprocal
+    // (1 ulp; no IEEE division sequence); computed for every row and then
+    // selected, so that no branch surrounds it
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       // rows past L must keep g = 0 and beta = 0 (no decay, no write)
       const bool live = r0 + i < it.L;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        gx[i][e] = live ? -5.f / (1.f + __builtin_amdgcn_exp2f(-av[i][e] * kLog2e))
-                        : 0.f;
-      bt[i] = live ? 1.f / (1.f + __builtin_amdgcn_exp2f(-bt[i] * kLog2e))
-                   : 0.f;
+      for (int e = 0; e < 8; ++e) {
+        const float sg = __builtin_amdgcn_rcpf(
+            1.f + __builtin_amdgcn_exp2f(-av[i][e] * kLog2e));
+        gx[i][e] = live ? -5.f * sg : 0.f;
+      }
+      const float sb = __builtin_amdgcn_rcpf(
+          1.f + __builtin_amdgcn_exp2f(-bt[i] * kLog2e));
+      bt[i] = live ? sb : 0.f;
     }
     __syncthreads();  // taps staged
     auto conv_rows = [&](const Raw8<Tin> (&win)[NWIN], int x, bool normalise,
