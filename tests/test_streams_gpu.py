@@ -65,3 +65,53 @@ def test_two_streams_equal_one_stream():
         assert torch.equal(ob, ob2) and torch.equal(sb, sb2), rep
         assert torch.equal(od, od2) and torch.equal(st, st2), rep
     U.log("   3 concurrent repetitions equal the sequential results")
+
+
+def test_graph_replay_equals_eager():
+    """A prefill and a decode step captured in one HIP graph: every replay,
+    with eager work and synchronisations between replays, gives the eager
+    results bit for bit (the library issues kernel launches only, no
+    memset or allocation, so it can be captured)."""
+    pa = inputs.make("prefill", seed=64, B=1, T=1000, H=8, s0=True)
+    pd = inputs.make("decode", seed=65, B=16, H=8)
+    q, k, v, g, beta, s0 = _prefill_dev(pa)
+    dq, dk, dv = (U.to_dev(x, pd.dtype) for x in (pd.q, pd.k, pd.v))
+    dg, dbeta = U.f32_dev(pd.g), U.f32_dev(pd.beta)
+    dstate0 = U.f32_dev(pd.initial_state)
+    o = torch.empty_like(v)
+    fs = torch.empty_like(s0)
+    ws = kda.workspace_for(1, 1000, 8, 128, 128, 64, U.DEV)
+    od = torch.empty_like(dv)
+    state = dstate0.clone()
+
+    def step():
+        kda.kda_prefill_chunked(q, k, v, g, beta, s0, chunk_size=64, o=o,
+                                final_state=fs, workspace=ws)
+        kda.kda_decode_step(dq, dk, dv, dg, dbeta, state, o=od)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (o, fs, od, state)]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):       # warm-up on a side stream
+        state.copy_(dstate0)
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    state.copy_(dstate0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        o.zero_(); fs.zero_(); od.zero_()
+        state.copy_(dstate0)             # the decode step updates in place
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((o, fs, od, state), ref):
+            assert torch.equal(got, want), rep
+    U.log("   4 graph replays equal the eager step")
