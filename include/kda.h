@@ -82,7 +82,8 @@ const char* kda_status_string(int32_t status);
 
 /*
  * Bytes of device workspace that the prefill entry points (kda_prefill_chunked,
- * kda_prefill_varlen and its _ckpt, _prologue, _prep and _recur forms) need
+ * kda_prefill_varlen and its _ckpt, _ckpt_at, _prologue, _prep and _recur
+ * forms) need
  * for N sequences holding total_T tokens (fixed length: N = B,
  * total_T = B*T).  The workspace holds, per head and chunk, the chunk-prep
  * kernel's outputs that the chunk-recurrence kernel consumes ("FlashKDA
@@ -126,7 +127,12 @@ kda_status_t kda_prefill_chunked(const void* q, const void* k, const void* v,
  *   q, k, g       [total_T, H, Dk]; v, o [total_T, H, Dv]; beta [total_T, H]
  *   cu_seqlens    DEVICE int32 [N+1], cu[0] = 0, non-decreasing,
  *                 cu[N] = total_T (read only by the kernels; no host sync)
- *   max_seqlen    host int >= every sequence length (sizes the launch grid)
+ *   max_seqlen    host int >= every sequence length (sizes the launch
+ *                 grid).  Not checked against cu_seqlens (that would need a
+ *                 device-to-host copy): a sequence longer than max_seqlen has
+ *                 only its first ceil(max_seqlen / C) * C tokens processed;
+ *                 outputs past them are left unwritten and its final state is
+ *                 the state after them.
  *   initial_state [N, H, Dk, Dv] fp32 or NULL; final_state [N, H, Dk, Dv]
  *                 fp32 or NULL, may alias initial_state.  A sequence of
  *                 length 0 gets its initial state (or zeros) as final state.
@@ -204,6 +210,43 @@ kda_status_t kda_prefill_varlen_ckpt(
     void* o, int32_t H, int32_t Dk, int32_t Dv, int32_t C, float scale,
     int32_t dtype, int32_t ckpt_every, float* ckpt_states, size_t ckpt_bytes,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_prefill_varlen that also stores the recurrent state at positions the
+ * caller lists for each sequence ("Kimi K3: The Manos, The Mythos, The
+ * Legendos", section "KDA prefix cache management": the fixed-size state is
+ * saved at a coarse interval and at prompt boundaries, so that a later
+ * request sharing a prefix can resume from the nearest saved state; here the
+ * caller chooses the positions, for example every 32K tokens plus the ends
+ * of the earlier turns' prompts inside a packed sequence).
+ *   ckpt_pos      DEVICE int32 [n_ckpt]: token counts p, within the
+ *                 sequence, after which to save the state.  Sequence n's
+ *                 positions are ckpt_pos[cu_ckpt[n] .. cu_ckpt[n+1]-1], in
+ *                 increasing order; each must be a multiple of C or equal to
+ *                 the sequence's length, with 1 <= p <= length.
+ *   cu_ckpt       DEVICE int32 [N+1]: cu_ckpt[0] = 0, non-decreasing,
+ *                 cu_ckpt[N] = n_ckpt (read only by the kernels).
+ *   n_ckpt        host int >= 0, the number of positions
+ *   ckpt_states   [n_ckpt, H, Dk, Dv] fp32: the state after position j's p
+ *                 tokens goes to slot j.  May be NULL when n_ckpt == 0.
+ *   ckpt_bytes    size of the ckpt_states buffer in bytes
+ * Positions that break the rules above are device-side precondition
+ * violations: they are skipped (their slots are left untouched), never
+ * written out of bounds; cu_ckpt values are clamped into [0, n_ckpt].
+ * The state at the end of each sequence is also final_state, as in
+ * kda_prefill_varlen.  All other arguments, and every error, as
+ * kda_prefill_varlen; n_ckpt < 0, NULL or misaligned ckpt_pos / cu_ckpt
+ * with n_ckpt > 0, or a ckpt_states buffer that is too small or misaligned,
+ * returns KDA_ERR_INVALID_ARG.
+ */
+kda_status_t kda_prefill_varlen_ckpt_at(
+    const void* q, const void* k, const void* v, const float* g,
+    const float* beta, const int32_t* cu_seqlens, int32_t N, int64_t total_T,
+    int32_t max_seqlen, const float* initial_state, float* final_state,
+    void* o, int32_t H, int32_t Dk, int32_t Dv, int32_t C, float scale,
+    int32_t dtype, const int32_t* ckpt_pos, const int32_t* cu_ckpt,
+    int32_t n_ckpt, float* ckpt_states, size_t ckpt_bytes, void* workspace,
+    size_t workspace_bytes, void* stream);
 
 /*
  * kda_prefill_varlen with the block's input prologue fused into the

@@ -28,7 +28,6 @@ kda_status_t check_prefill_common(int32_t H, int32_t Dk, int32_t Dv,
     return KDA_ERR_UNSUPPORTED;
   if (!supported_dims(Dk, Dv) || !supported_chunk(C))
     return KDA_ERR_UNSUPPORTED;
-  if (H > 65535) return KDA_ERR_UNSUPPORTED;  // grid y of the prep launch
   return KDA_OK;
 }
 
@@ -73,7 +72,54 @@ kda_status_t check_tensors(int64_t tokens, const void* q, const void* k,
   return KDA_OK;
 }
 
-// Varlen prefill, with state checkpoints when want_ckpt.
+// State checkpoints requested by a prefill call: none, every `every` tokens
+// of each sequence, or at the listed positions (see kda.h).
+struct CkptOpts {
+  enum Mode { kNone, kEvery, kList } mode = kNone;
+  int32_t every = 0;
+  const int32_t* pos = nullptr;
+  const int32_t* cu = nullptr;
+  int32_t n = 0;
+  float* states = nullptr;
+  size_t bytes = 0;
+};
+
+// Validates the checkpoint request and fills its part of the launch args.
+kda_status_t set_ckpt(const CkptOpts& ck, int64_t total_T, int32_t H,
+                      int32_t Dk, int32_t Dv, int32_t C, kda::PrefillArgs& a) {
+  a.ckpt_states = nullptr;
+  a.ckpt_every = 0;
+  a.ckpt_pos = nullptr;
+  a.cu_ckpt = nullptr;
+  a.n_ckpt = 0;
+  if (ck.mode == CkptOpts::kNone) return KDA_OK;
+  int64_t slots = 0;
+  if (ck.mode == CkptOpts::kEvery) {
+    if (ck.every <= 0 || ck.every % C != 0) return KDA_ERR_INVALID_ARG;
+    slots = total_T / ck.every;
+  } else {
+    if (ck.n < 0) return KDA_ERR_INVALID_ARG;
+    slots = ck.n;
+    if (slots > 0 && (!ck.pos || !ck.cu || !aligned(ck.pos, 4) ||
+                      !aligned(ck.cu, 4)))
+      return KDA_ERR_INVALID_ARG;
+  }
+  if (slots == 0) return KDA_OK;  // no checkpoint can be written
+  if (!ck.states || !aligned(ck.states, 16)) return KDA_ERR_INVALID_ARG;
+  const double need = (double)slots * H * Dk * Dv * 4.0;
+  if (need > 9.0e18 || (double)ck.bytes < need) return KDA_ERR_INVALID_ARG;
+  a.ckpt_states = ck.states;
+  if (ck.mode == CkptOpts::kEvery) {
+    a.ckpt_every = ck.every;
+  } else {
+    a.ckpt_pos = ck.pos;
+    a.cu_ckpt = ck.cu;
+    a.n_ckpt = ck.n;
+  }
+  return KDA_OK;
+}
+
+// Varlen prefill, with the requested state checkpoints.
 kda_status_t prefill_varlen(const void* q, const void* k, const void* v,
                             const float* g, const float* beta,
                             const int32_t* cu_seqlens, int32_t N,
@@ -81,16 +127,13 @@ kda_status_t prefill_varlen(const void* q, const void* k, const void* v,
                             const float* initial_state, float* final_state,
                             void* o, int32_t H, int32_t Dk, int32_t Dv,
                             int32_t C, float scale, int32_t dtype,
-                            bool want_ckpt, int32_t ckpt_every,
-                            float* ckpt_states, size_t ckpt_bytes,
-                            const float* conv_w, void* workspace,
-                            size_t workspace_bytes, void* stream,
-                            int stages = kStagesBoth) {
+                            const CkptOpts& ck, const float* conv_w,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream, int stages = kStagesBoth) {
   if (N <= 0 || total_T < 0 || max_seqlen < 0) return KDA_ERR_INVALID_ARG;
   if (total_T > 0 && max_seqlen == 0) return KDA_ERR_INVALID_ARG;
   kda_status_t st = check_prefill_common(H, Dk, Dv, C, dtype);
   if (st != KDA_OK) return st;
-  if (N > 65535) return KDA_ERR_UNSUPPORTED;
   if (!cu_seqlens || !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARG;
   if (stages == kStagesBoth) {
     st = check_tensors(total_T, q, k, v, g, beta, o);
@@ -107,17 +150,10 @@ kda_status_t prefill_varlen(const void* q, const void* k, const void* v,
   if ((int64_t)(Dv / 16) * H * N > INT_MAX)
     return KDA_ERR_UNSUPPORTED;
   const int64_t maxlen = max_seqlen < total_T ? max_seqlen : total_T;
-  if (want_ckpt) {
-    if (ckpt_every <= 0 || ckpt_every % C != 0) return KDA_ERR_INVALID_ARG;
-    const int64_t slots = total_T / ckpt_every;
-    if (slots > 0) {
-      if (!ckpt_states || !aligned(ckpt_states, 16)) return KDA_ERR_INVALID_ARG;
-      const double need = (double)slots * H * Dk * Dv * 4.0;
-      if (need > 9.0e18 || (double)ckpt_bytes < need) return KDA_ERR_INVALID_ARG;
-    }
-  }
 
   kda::PrefillArgs a{};
+  st = set_ckpt(ck, total_T, H, Dk, Dv, C, a);
+  if (st != KDA_OK) return st;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.cu_seqlens = cu_seqlens;
   a.T_fixed = 0;
@@ -129,9 +165,6 @@ kda_status_t prefill_varlen(const void* q, const void* k, const void* v,
   a.o = o;
   a.H = H;
   a.scale = scale;
-  a.ckpt_every = want_ckpt ? ckpt_every : 0;
-  a.ckpt_states =
-      (want_ckpt && total_T / ckpt_every > 0) ? ckpt_states : nullptr;
   a.conv_w = conv_w;
   return run_prefill(a, Dk, C, dtype, workspace, workspace_bytes, stream,
                      stages);
@@ -205,7 +238,6 @@ kda_status_t kda_prefill_chunked(const void* q, const void* k, const void* v,
   if (B <= 0 || T < 0) return KDA_ERR_INVALID_ARG;
   kda_status_t st = check_prefill_common(H, Dk, Dv, C, dtype);
   if (st != KDA_OK) return st;
-  if (B > 65535) return KDA_ERR_UNSUPPORTED;  // grid z of the prep launch
   const int64_t total = (int64_t)B * T;
   st = check_tensors(total, q, k, v, g, beta, o);
   if (st != KDA_OK) return st;
@@ -241,7 +273,7 @@ kda_status_t kda_prefill_varlen(const void* q, const void* k, const void* v,
                                 size_t workspace_bytes, void* stream) {
   return prefill_varlen(q, k, v, g, beta, cu_seqlens, N, total_T, max_seqlen,
                         initial_state, final_state, o, H, Dk, Dv, C, scale,
-                        dtype, false, 0, nullptr, 0, nullptr, workspace,
+                        dtype, CkptOpts{}, nullptr, workspace,
                         workspace_bytes, stream);
 }
 
@@ -255,8 +287,8 @@ kda_status_t kda_prefill_varlen_prep(const void* q, const void* k,
                                      size_t workspace_bytes, void* stream) {
   return prefill_varlen(q, k, v, g, beta, cu_seqlens, N, total_T, max_seqlen,
                         nullptr, nullptr, nullptr, H, Dk, Dv, C, 1.0f, dtype,
-                        false, 0, nullptr, 0, nullptr, workspace,
-                        workspace_bytes, stream, kStagePrep);
+                        CkptOpts{}, nullptr, workspace, workspace_bytes,
+                        stream, kStagePrep);
 }
 
 kda_status_t kda_prefill_varlen_recur(const int32_t* cu_seqlens, int32_t N,
@@ -269,8 +301,8 @@ kda_status_t kda_prefill_varlen_recur(const int32_t* cu_seqlens, int32_t N,
                                       void* stream) {
   return prefill_varlen(nullptr, nullptr, nullptr, nullptr, nullptr,
                         cu_seqlens, N, total_T, max_seqlen, initial_state,
-                        final_state, o, H, Dk, Dv, C, scale, dtype, false, 0,
-                        nullptr, 0, nullptr, workspace, workspace_bytes,
+                        final_state, o, H, Dk, Dv, C, scale, dtype,
+                        CkptOpts{}, nullptr, workspace, workspace_bytes,
                         stream, kStageRecur);
 }
 
@@ -281,10 +313,36 @@ kda_status_t kda_prefill_varlen_ckpt(
     void* o, int32_t H, int32_t Dk, int32_t Dv, int32_t C, float scale,
     int32_t dtype, int32_t ckpt_every, float* ckpt_states, size_t ckpt_bytes,
     void* workspace, size_t workspace_bytes, void* stream) {
+  CkptOpts ck;
+  ck.mode = CkptOpts::kEvery;
+  ck.every = ckpt_every;
+  ck.states = ckpt_states;
+  ck.bytes = ckpt_bytes;
   return prefill_varlen(q, k, v, g, beta, cu_seqlens, N, total_T, max_seqlen,
                         initial_state, final_state, o, H, Dk, Dv, C, scale,
-                        dtype, true, ckpt_every, ckpt_states, ckpt_bytes,
-                        nullptr, workspace, workspace_bytes, stream);
+                        dtype, ck, nullptr, workspace, workspace_bytes,
+                        stream);
+}
+
+kda_status_t kda_prefill_varlen_ckpt_at(
+    const void* q, const void* k, const void* v, const float* g,
+    const float* beta, const int32_t* cu_seqlens, int32_t N, int64_t total_T,
+    int32_t max_seqlen, const float* initial_state, float* final_state,
+    void* o, int32_t H, int32_t Dk, int32_t Dv, int32_t C, float scale,
+    int32_t dtype, const int32_t* ckpt_pos, const int32_t* cu_ckpt,
+    int32_t n_ckpt, float* ckpt_states, size_t ckpt_bytes, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  CkptOpts ck;
+  ck.mode = CkptOpts::kList;
+  ck.pos = ckpt_pos;
+  ck.cu = cu_ckpt;
+  ck.n = n_ckpt;
+  ck.states = ckpt_states;
+  ck.bytes = ckpt_bytes;
+  return prefill_varlen(q, k, v, g, beta, cu_seqlens, N, total_T, max_seqlen,
+                        initial_state, final_state, o, H, Dk, Dv, C, scale,
+                        dtype, ck, nullptr, workspace, workspace_bytes,
+                        stream);
 }
 
 kda_status_t kda_prefill_varlen_prologue(
@@ -297,7 +355,7 @@ kda_status_t kda_prefill_varlen_prologue(
   if (!conv_w || !aligned(conv_w, 16)) return KDA_ERR_INVALID_ARG;
   return prefill_varlen(xq, xk, xv, a, b, cu_seqlens, N, total_T, max_seqlen,
                         initial_state, final_state, o, H, Dk, Dv, C, scale,
-                        dtype, false, 0, nullptr, 0, conv_w, workspace,
+                        dtype, CkptOpts{}, conv_w, workspace,
                         workspace_bytes, stream);
 }
 

@@ -19,7 +19,6 @@
 // state is touched exactly once per step, so its loads and stores may carry
 // the non-temporal cache policy (kNt) to keep it from displacing other data
 // in the caches.
-#include <stdlib.h>
 
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
@@ -182,51 +181,21 @@ void decode_kernel(DecodeArgs a) {
 
 }
 
-// Launch shape: threads per workgroup (capped by D^2 / 4, one float4 per
-// thread and row group) and the cache policy of the state accesses.  At
-// D = 128, 1024 threads hold 4 rows each in 60 VGPRs, so two workgroups
-// (128 KB of state loads) are in flight per CU.
-// KDA_DECODE_THREADS (256, 512, 1024) and KDA_DECODE_NT (0, 1) override the
-// defaults for tuning sweeps.
-struct DecodeShape {
-  int threads;
-  bool nt;
-};
-
-DecodeShape decode_shape() {
-  static const DecodeShape shape = [] {
-    DecodeShape d{1024, true};
-    if (const char* e = getenv("KDA_DECODE_THREADS")) {
-      const int t = atoi(e);
-      if (t == 256 || t == 512 || t == 1024) d.threads = t;
-    }
-    if (const char* e = getenv("KDA_DECODE_NT")) d.nt = atoi(e) != 0;
-    return d;
-  }();
-  return shape;
-}
-
-template <typename Tio, int D, int NT>
-hipError_t launch_nt(const DecodeArgs& a, bool nt, hipStream_t st) {
-  constexpr int T = (D * D / 4) < NT ? (D * D / 4) : NT;
-  const unsigned blocks = (unsigned)a.B * (unsigned)a.H;
-  if (a.z)  // fused output epilogue: default cache policy shape only
-    return launch_kernel(decode_kernel<Tio, D, T, true, true>, dim3(blocks),
-                         dim3(T), st, a);
-  return nt ? launch_kernel(decode_kernel<Tio, D, T, true, false>,
-                            dim3(blocks), dim3(T), st, a)
-            : launch_kernel(decode_kernel<Tio, D, T, false, false>,
-                            dim3(blocks), dim3(T), st, a);
-}
-
+// Launch shape: one float4 per thread and row group, at most 1024 threads
+// per workgroup (D^2 / 4 below D = 64).  At D = 128, 1024 threads hold 4 rows
+// each in 60 VGPRs, so two workgroups (128 KB of state loads) are in flight
+// per CU.  The state is touched once per step, so its accesses carry the
+// non-temporal policy (measured: the kernel's own time then covers all of
+// its traffic, and back-to-back steps run at the streaming ceiling).
 template <typename Tio, int D>
 hipError_t launch(const DecodeArgs& a, hipStream_t st) {
-  const DecodeShape sh = decode_shape();
-  switch (sh.threads) {
-    case 512: return launch_nt<Tio, D, 512>(a, sh.nt, st);
-    case 1024: return launch_nt<Tio, D, 1024>(a, sh.nt, st);
-  }
-  return launch_nt<Tio, D, 256>(a, sh.nt, st);
+  constexpr int T = (D * D / 4) < 1024 ? (D * D / 4) : 1024;
+  const unsigned blocks = (unsigned)a.B * (unsigned)a.H;
+  if (a.z)  // fused output epilogue
+    return launch_kernel(decode_kernel<Tio, D, T, true, true>, dim3(blocks),
+                         dim3(T), st, a);
+  return launch_kernel(decode_kernel<Tio, D, T, true, false>, dim3(blocks),
+                       dim3(T), st, a);
 }
 
 template <typename Tio>

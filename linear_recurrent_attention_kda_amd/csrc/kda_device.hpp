@@ -258,4 +258,85 @@ __device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int n,
   }
 }
 
+// Chunks of sequence [bos, eos) that the recurrence walks: never more than
+// the chunk-prep grid covered (max_chunks, from the caller's max_seqlen), so
+// a max_seqlen below a sequence's length leaves that sequence's later tokens
+// unprocessed instead of reading workspace slots nobody wrote.
+__device__ __forceinline__ int64_t seq_chunks(const PrefillArgs& a,
+                                              int64_t bos, int64_t eos,
+                                              int C) {
+  const int64_t n = (eos - bos + C - 1) / C;
+  return n < a.max_chunks ? n : a.max_chunks;
+}
+
+// State checkpoints of one sequence ("Kimi K3: The Manos, The Mythos, The
+// Legendos", section "KDA prefix cache management": the fixed-size state is
+// saved every so many tokens and at prompt boundaries).  The recurrence
+// holds the state at every chunk boundary.  After each chunk it asks
+// `due(done)`, with `done` the tokens of the sequence processed so far (a
+// multiple of C, or the sequence length after a partial last chunk), and
+// while that is true stores the state to `slot` and calls `next()`.  Every
+// member has the same value in all threads of the workgroup.
+struct CkptCursor {
+  static constexpr int64_t kNone = INT64_MAX;
+  const int32_t* pos;  // list mode: ckpt_pos; interval mode: nullptr
+  int64_t at;          // tokens done at the pending checkpoint, or kNone
+  int64_t slot;        // its slot in ckpt_states
+  int64_t len;         // tokens of the sequence
+  int32_t every;       // interval mode: the interval
+  int32_t j, jend;     // list mode: pending entry of pos, end of the entries
+
+  __device__ __forceinline__ void init(const PrefillArgs& a, int n,
+                                       int64_t bos, int64_t eos) {
+    pos = a.ckpt_pos;
+    len = eos - bos;
+    every = a.ckpt_every;
+    if (pos) {
+      // this sequence's entries, clamped into [0, n_ckpt]
+      int32_t b = a.cu_ckpt[n], e = a.cu_ckpt[n + 1];
+      b = b < 0 ? 0 : (b > a.n_ckpt ? a.n_ckpt : b);
+      e = e < b ? b : (e > a.n_ckpt ? a.n_ckpt : e);
+      j = __builtin_amdgcn_readfirstlane(b);
+      jend = __builtin_amdgcn_readfirstlane(e);
+      load();
+    } else {
+      j = jend = 0;
+      at = every <= len ? every : kNone;
+      slot = (bos + every) / every - 1;
+    }
+  }
+  // True when a checkpoint falls exactly at `done` tokens.  List entries
+  // that were passed without an exact match (not a multiple of C and not the
+  // sequence length, out of increasing order, or <= 0) are skipped and their
+  // slots left untouched.
+  __device__ __forceinline__ bool due(int64_t done) {
+    if (pos) {
+      while (at < done) {
+        ++j;
+        load();
+      }
+    }
+    return at == done;
+  }
+  __device__ __forceinline__ void next() {
+    if (pos) {
+      ++j;
+      load();
+    } else {
+      at = at + every <= len ? at + every : kNone;
+      slot += 1;
+    }
+  }
+
+ private:
+  __device__ __forceinline__ void load() {
+    if (j < jend) {
+      at = __builtin_amdgcn_readfirstlane(pos[j]);
+      slot = j;
+    } else {
+      at = kNone;
+    }
+  }
+};
+
 }  // namespace kda

@@ -83,7 +83,14 @@ struct PrefillArgs {
   char* ws;
   int64_t nslots;
   float* ckpt_states;          // state checkpoints, or nullptr
-  int32_t ckpt_every;          // checkpoint interval in tokens (multiple of C)
+  // Where the checkpoints fall.  Interval mode (ckpt_pos == nullptr): every
+  // ckpt_every tokens of each sequence (a multiple of C).  List mode: the
+  // positions ckpt_pos[cu_ckpt[n] .. cu_ckpt[n+1]-1] (device int32) of
+  // sequence n, checkpoint j going to slot j of ckpt_states [n_ckpt, ...].
+  int32_t ckpt_every;
+  const int32_t* ckpt_pos;
+  const int32_t* cu_ckpt;
+  int32_t n_ckpt;
   // Input prologue fused into the chunk-prep kernel when conv_w != nullptr:
   // q, k, v then hold the short convolutions' inputs, g the decay gate's
   // pre-activation a (g = -5 sigmoid(a)) and beta the pre-activation b

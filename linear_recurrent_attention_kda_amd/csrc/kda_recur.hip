@@ -21,7 +21,7 @@
 // MI355X consecutive workgroup ids go round-robin over the 8 XCDs (each with
 // its own L2); ids are remapped so that the slices of one head run on one
 // XCD and share its L2 copy of the head's chunk tensors.
-#include <stdlib.h>
+#include <atomic>
 
 #include "kda_device.hpp"
 
@@ -130,8 +130,10 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
     }
   }
 
-  const int64_t nchunks = (eos - bos + C - 1) / C;
+  const int64_t nchunks = seq_chunks(a, bos, eos, C);
   const char* ws_head = a.ws + (size_t)h * a.nslots * lay.block_bytes;
+  CkptCursor ck;
+  if (kCkpt) ck.init(a, n, bos, eos);
 
   // Loads of chunk ci's operands, in three groups issued as soon as the
   // registers they fill are free: W, Q^ and U~ (read by the U phase), M (the
@@ -316,14 +318,13 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
         *reinterpret_cast<bf16x4*>(&s_SbT[16 * jt + rl][16 * ct + 4 * kg]) = sb;
       }
     }
-    // state checkpoint after this chunk: "Kimi K3: The Manos, The Mythos,
-    // The Legendos", section "KDA prefix cache management" (the state saved
-    // every so many tokens).  The condition is uniform over the workgroup.
+    // state checkpoints after this chunk: "Kimi K3: The Manos, The Mythos,
+    // The Legendos", section "KDA prefix cache management".  The condition
+    // is uniform over the workgroup.
     if (kCkpt) {
-      const int64_t p = (ci + 1) * C;  // tokens of the sequence done
-      if (p % a.ckpt_every == 0 && p <= eos - bos) {
-        const int64_t cslot = (bos + p) / a.ckpt_every - 1;
-        float* dst = a.ckpt_states + ((size_t)cslot * H + h) * (size_t)K * V;
+      const int64_t done = (ci + 1) * C < eos - bos ? (ci + 1) * C : eos - bos;
+      while (ck.due(done)) {
+        float* dst = a.ckpt_states + ((size_t)ck.slot * H + h) * (size_t)K * V;
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
           const int t = s0t + i;
@@ -335,6 +336,7 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
                   S[i][e];
           }
         }
+        ck.next();
       }
     }
     load_s(op, nb);
@@ -461,7 +463,7 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
   int64_t bos, eos;
   seq_bounds(a, n, bos, eos);
   const WsLayout lay = WsLayout::make(C, K, V);
-  const int64_t nchunks = (eos - bos + C - 1) / C;
+  const int64_t nchunks = seq_chunks(a, bos, eos, C);
   const char* ws_head = a.ws + (size_t)h * a.nslots * lay.block_bytes;
   auto chunk_ptr = [&](int64_t ci) {
     ci = ci < nchunks ? ci : nchunks - 1;  // past the end: a harmless reload
@@ -522,6 +524,8 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
   }
 
   // ---- compute waves ----------------------------------------------------
+  CkptCursor ck;
+  if (kCkpt) ck.init(a, n, bos, eos);
   const int rl = lane & 15, kg = lane >> 4;
   const int u0 = wave * UPW;
   const int mrow = u0 / JT;
@@ -652,12 +656,11 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
       for (int e = 0; e < 4; ++e) sb[e] = (bf16)S[i][e];
       *reinterpret_cast<bf16x4*>(&s_SbT[16 * jt + rl][16 * ct + 4 * kg]) = sb;
     }
-    // state checkpoint after this chunk (uniform over the workgroup)
+    // state checkpoints after this chunk (uniform over the workgroup)
     if (kCkpt) {
-      const int64_t p = (ci + 1) * C;
-      if (p % a.ckpt_every == 0 && p <= eos - bos) {
-        const int64_t cslot = (bos + p) / a.ckpt_every - 1;
-        float* dst = a.ckpt_states + ((size_t)cslot * H + h) * (size_t)K * V;
+      const int64_t done = (ci + 1) * C < eos - bos ? (ci + 1) * C : eos - bos;
+      while (ck.due(done)) {
+        float* dst = a.ckpt_states + ((size_t)ck.slot * H + h) * (size_t)K * V;
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
           const int t = s0t + i;
@@ -667,6 +670,7 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
             dst[(size_t)(16 * ct + 4 * kg + e) * V + j0 + 16 * jt + rl] =
                 S[i][e];
         }
+        ck.next();
       }
     }
   }
@@ -684,77 +688,74 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
   }
 }
 
+// Compute units of the current device, queried once per device and cached
+// (the query is not repeated on every launch).
+inline int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return 256;
+  int cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                              dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
+
 // Slice width.  Wider slices re-read the per-chunk tensors fewer times and
 // do more matrix work per chunk loaded; narrower ones give more workgroups
 // when there are few (sequence, head) pairs.  Measured on MI355X: 96 heads
-// run fastest at 64 (192 workgroups), 32 heads at 16 (256 workgroups).
-// KDA_RECUR_BV (16 / 32 / 64 / 128) overrides the choice.
+// run fastest at 64 (192 workgroups), 32 heads at 16 (256 workgroups);
+// 128-wide slices were slower on both.
 inline int pick_bv(int D, int64_t units) {
-  static const int forced = [] {
-    const char* e = getenv("KDA_RECUR_BV");
-    return e ? atoi(e) : 0;
-  }();
-  int cus = 256;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
-                            dev) != hipSuccess)
-    cus = 256;
+  const int cus = device_cus();
   int bv = 16;
   if (D >= 64 && units * (D / 64) >= cus / 2)
     bv = 64;
   else if (D >= 32 && units * (D / 32) >= cus)
     bv = 32;
-  if ((forced == 16 || forced == 32 || forced == 64 || forced == 128) &&
-      forced <= D)
-    bv = forced;
   return D == 16 ? 16 : bv;
 }
 
 // Two register operand sets in flight and 4 waves per workgroup: a third
 // set, or 8 waves (also with the outputs' products given to their own
 // waves), measured no faster on MI355X.
-// Variant choice for D = 128, C = 64.  Measured on MI355X: the streamed
-// variant runs the 96-head prefill workload (64-wide slices) in 287 us
-// against 301 us, and the 32-head long workload (16-wide slices) 4 % slower.
-// KDA_RECUR_STREAM=0 / 1 forces the choice for tuning sweeps.
-inline bool use_stream(int bv) {
-  static const int forced = [] {
-    const char* e = getenv("KDA_RECUR_STREAM");
-    return e ? (atoi(e) != 0 ? 1 : 0) : -1;
-  }();
-  return forced >= 0 ? forced == 1 : bv == 64;
-}
-
+// Variant choice for D = 128, C = 64: the streamed variant serves the
+// 64-wide slices.  Measured on MI355X: it runs the 96-head prefill workload
+// (64-wide slices) in 287 us against 301 us, and the 32-head long workload
+// (16-wide slices) 4 % slower.
 template <typename Tout, int D, int C, int BV>
 hipError_t launch_w(const PrefillArgs& a, hipStream_t st) {
   const unsigned blocks = (unsigned)(D / BV) * (unsigned)a.H * (unsigned)a.N;
-  if constexpr (D == 128 && C == 64 && BV <= 64) {
-    if (use_stream(BV))
-      return a.ckpt_states
-                 ? launch_kernel(recur_stream_kernel<Tout, D, C, BV, true>,
-                                 dim3(blocks), dim3(320), st, a)
-                 : launch_kernel(recur_stream_kernel<Tout, D, C, BV, false>,
-                                 dim3(blocks), dim3(320), st, a);
+  // state checkpoints: their own compile-time variant of each kernel
+  if constexpr (D == 128 && C == 64 && BV == 64) {
+    return a.ckpt_states
+               ? launch_kernel(recur_stream_kernel<Tout, D, C, BV, true>,
+                               dim3(blocks), dim3(320), st, a)
+               : launch_kernel(recur_stream_kernel<Tout, D, C, BV, false>,
+                               dim3(blocks), dim3(320), st, a);
+  } else {
+    return a.ckpt_states
+               ? launch_kernel(recur_kernel<Tout, D, C, BV, 2, 4, true>,
+                               dim3(blocks), dim3(256), st, a)
+               : launch_kernel(recur_kernel<Tout, D, C, BV, 2, 4, false>,
+                               dim3(blocks), dim3(256), st, a);
   }
-  // state checkpoints: their own kernel variant
-  return a.ckpt_states
-             ? launch_kernel(recur_kernel<Tout, D, C, BV, 2, 4, true>,
-                             dim3(blocks), dim3(256), st, a)
-             : launch_kernel(recur_kernel<Tout, D, C, BV, 2, 4, false>,
-                             dim3(blocks), dim3(256), st, a);
 }
 
+// Only the slice widths pick_bv can return are instantiated: 64 or 16 at
+// D = 128 and 64, 32 or 16 at D = 32, 16 at D = 16.
 template <typename Tout, int D, int C>
 hipError_t launch(const PrefillArgs& a, hipStream_t st) {
   const int bv = pick_bv(D, (int64_t)a.N * a.H);
-  if constexpr (D >= 128) {
-    if (bv == 128) return launch_w<Tout, D, C, 128>(a, st);
-  }
   if constexpr (D >= 64) {
     if (bv == 64) return launch_w<Tout, D, C, 64>(a, st);
-  }
-  if constexpr (D >= 32) {
+  } else if constexpr (D == 32) {
     if (bv == 32) return launch_w<Tout, D, C, 32>(a, st);
   }
   return launch_w<Tout, D, C, 16>(a, st);

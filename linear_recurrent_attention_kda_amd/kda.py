@@ -75,6 +75,10 @@ def load() -> ctypes.CDLL:
         lib.kda_prefill_varlen_ckpt.argtypes = [
             vp, vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, i32,
             i32, f32, i32, i32, vp, sz, vp, sz, vp]
+        lib.kda_prefill_varlen_ckpt_at.restype = i32
+        lib.kda_prefill_varlen_ckpt_at.argtypes = [
+            vp, vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, i32,
+            i32, f32, i32, vp, vp, i32, vp, sz, vp, sz, vp]
         lib.kda_spec_verify.restype = i32
         lib.kda_spec_verify.argtypes = [
             vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
@@ -362,6 +366,65 @@ def kda_prefill_varlen_ckpt(q, k, v, g, beta, cu_seqlens, max_seqlen: int,
         _stream(dev))
     if st != KDA_OK:
         raise KDAError("kda_prefill_varlen_ckpt", st)
+    return o, final_state, ckpt_states
+
+
+def kda_prefill_varlen_ckpt_at(q, k, v, g, beta, cu_seqlens,
+                               max_seqlen: int, initial_state=None, *,
+                               ckpt_pos, cu_ckpt, chunk_size: int = 64,
+                               scale: float = 1.0,
+                               output_final_state: bool = True,
+                               final_state=None, o=None, ckpt_states=None,
+                               workspace=None):
+    """kda_prefill_varlen that also stores the state at caller-given token
+    positions: sequence n's positions are ckpt_pos[cu_ckpt[n]:cu_ckpt[n+1]]
+    (device int32, increasing, each a multiple of chunk_size or the
+    sequence's length).  Returns (o, final_state, ckpt_states) with
+    ckpt_states [len(ckpt_pos), H, Dk, Dv] fp32, slot j holding the state
+    after position j; slots of positions that break the rules are left as
+    allocated (zeros)."""
+    lib = load()
+    total_T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    N = cu_seqlens.numel() - 1
+    n_ckpt = ckpt_pos.numel()
+    for t, n, s, dt in ((q, "q", (total_T, H, Dk), q.dtype),
+                        (k, "k", (total_T, H, Dk), q.dtype),
+                        (v, "v", (total_T, H, Dv), q.dtype),
+                        (g, "g", (total_T, H, Dk), torch.float32),
+                        (beta, "beta", (total_T, H), torch.float32),
+                        (cu_seqlens, "cu_seqlens", (N + 1,), torch.int32),
+                        (ckpt_pos, "ckpt_pos", (n_ckpt,), torch.int32),
+                        (cu_ckpt, "cu_ckpt", (N + 1,), torch.int32)):
+        _check(t, n, s, dt, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (N, H, Dk, Dv), torch.float32,
+               dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32,
+                                  device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (N, H, Dk, Dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((total_T, H, Dv), dtype=q.dtype, device=dev)
+    _check(o, "o", (total_T, H, Dv), q.dtype, dev)
+    if ckpt_states is None:
+        ckpt_states = torch.zeros((n_ckpt, H, Dk, Dv), dtype=torch.float32,
+                                  device=dev)
+    _check(ckpt_states, "ckpt_states", (n_ckpt, H, Dk, Dv), torch.float32,
+           dev)
+    if workspace is None:
+        workspace = workspace_for(N, total_T, H, Dk, Dv, chunk_size, dev)
+    st = lib.kda_prefill_varlen_ckpt_at(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N,
+        total_T, int(max_seqlen), _ptr(initial_state), _ptr(final_state),
+        _ptr(o), H, Dk, Dv, chunk_size, scale, _dtype_code(q),
+        _ptr(ckpt_pos) if n_ckpt > 0 else None, _ptr(cu_ckpt), n_ckpt,
+        _ptr(ckpt_states) if n_ckpt > 0 else None, ckpt_states.numel() * 4,
+        _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_prefill_varlen_ckpt_at", st)
     return o, final_state, ckpt_states
 
 

@@ -33,6 +33,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"kda_abi_version", "kda_status_string",
                           "kda_prefill_workspace_size", "kda_prefill_chunked",
                           "kda_prefill_varlen", "kda_prefill_varlen_ckpt",
+                          "kda_prefill_varlen_ckpt_at",
                           "kda_decode_step", "kda_spec_verify",
                           "kda_spec_commit", "kda_output_norm_gate",
                           "kda_decode_step_gated",
@@ -210,6 +211,38 @@ def test_prefill_varlen_ckpt_validation():
     assert _ckpt(lib, N=0) == INVALID
     assert _ckpt(lib, C=8, every=64) == UNSUP
     assert _ckpt(lib, ws_bytes=10) == WS
+
+
+def _ckpt_at(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, cu=P, N=2, total=300, maxlen=200,
+             s0=NULL, s1=NULL, o=P, H=2, Dk=64, Dv=64, C=32, scale=1.0,
+             dtype=0, pos=P, cuc=P, n=3, ck=P, ck_bytes=1 << 40, ws=P,
+             ws_bytes=1 << 40, stream=NULL)
+    a.update(kw)
+    return lib.kda_prefill_varlen_ckpt_at(
+        a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"],
+        a["total"], a["maxlen"], a["s0"], a["s1"], a["o"], a["H"], a["Dk"],
+        a["Dv"], a["C"], a["scale"], a["dtype"], a["pos"], a["cuc"], a["n"],
+        a["ck"], a["ck_bytes"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_prefill_varlen_ckpt_at_validation():
+    """Every call here fails validation (nothing is launched)."""
+    lib = kda.load()
+    assert _ckpt_at(lib, n=-1) == INVALID
+    assert _ckpt_at(lib, pos=NULL) == INVALID
+    assert _ckpt_at(lib, cuc=NULL) == INVALID
+    assert _ckpt_at(lib, pos=ctypes.c_void_p(0x100002)) == INVALID
+    assert _ckpt_at(lib, cuc=ctypes.c_void_p(0x100001)) == INVALID
+    assert _ckpt_at(lib, ck=NULL) == INVALID
+    assert _ckpt_at(lib, ck=ctypes.c_void_p(0x100004)) == INVALID
+    # 3 slots x 2 heads x 64 x 64 x 4 B = 98304 B needed
+    assert _ckpt_at(lib, ck_bytes=98303) == INVALID
+    # the checks shared with kda_prefill_varlen come first
+    assert _ckpt_at(lib, N=0) == INVALID
+    assert _ckpt_at(lib, C=8) == UNSUP
+    assert _ckpt_at(lib, ws_bytes=10) == WS
+    assert _ckpt_at(lib, ws=NULL) == WS
 
 
 def _verify(lib, **kw):
