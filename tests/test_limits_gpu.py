@@ -1,8 +1,8 @@
 """GPU parity at the edges of the supported sizes: very many heads (large
 token strides in the packed layout, fp32 inputs), very many short packed
 sequences, a large decode batch, and the longest speculative draft.  Each
-is compared with the fp64 oracle on sampled heads or sequences (heads and
-sequences are independent)."""
+is compared with the fp64 oracle on every head (prefill) or on sampled
+sequences (decode, whose sequences are independent)."""
 import numpy as np
 import pytest
 import torch
@@ -22,7 +22,7 @@ def test_many_heads_fp32_partial_chunk():
     spans 128 MB of each input; T = 130 ends in a partial chunk."""
     p = inputs.make("prefill", seed=51, B=1, T=130, H=4096, dtype="fp32",
                     s0=True)
-    U.check_prefill(p, heads=[0, 2047, 4095], label="4096 heads fp32")
+    U.check_prefill(p, label="4096 heads fp32", head_group=512)
 
 
 def test_thousand_short_sequences():
@@ -106,7 +106,8 @@ def test_inputs_beyond_4_gib():
             rep(base.q), rep(base.k), rep(base.v), rep(base.g),
             np.tile(base.beta[:, :, [h]], (1, rt, 1)),
             base.initial_state[:, [h]])
-        eo = U.prefill_o_rel(U.host(o[:, :, [dev_head]]), o_ref)
+        eo = max(U.prefill_o_rel(U.host(o[:, :, [dev_head]]), o_ref,
+                                 [0, T], base.C))
         es = U.slice_rel(U.host(s[:, [dev_head]]), s_ref, (0, 1))
         U.log("   head %d: o rel %.3e state rel %.3e" % (dev_head, eo, es))
         assert eo <= U.PREFILL_TOL and es <= U.PREFILL_TOL
