@@ -108,6 +108,23 @@ def mfma_figures(kernel_file: str, avg_ms: float):
                                (s * counts.CLOCK_HZ * counts.SIMDS), 4)}
 
 
+def kernel_entry(name, src_file, nbytes, ms, traffic=True):
+    """Roofline entry of one kernel: its algorithmic bytes per launch over
+    its average launch time (HIP events), against the HBM peak.  The stored
+    counter figures (traffic, MFMA) were taken on the 8K-token prefill and
+    decode workloads, so other workloads pass traffic=False."""
+    avg, med = float(np.mean(ms)), float(np.median(ms))
+    ach = nbytes / (avg * 1e-3) / 1e9
+    return {"kernel": name, "bound": "hbm", "achieved": round(ach, 2),
+            "peak": counts.HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(ach / counts.HBM_PEAK_GBPS, 4),
+            "traffic": read_traffic(src_file) if traffic else None,
+            "algorithmic_bytes_per_launch": nbytes,
+            "avg_launch_ms": round(avg, 5),
+            "median_launch_ms": round(med, 5),
+            "mfma": mfma_figures(src_file, avg) if traffic else None}
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -147,6 +164,10 @@ def main(argv=None):
                     help="skip the measurements taken after the timed steps "
                          "(back-to-back decode, reference copy), so that a "
                          "kernel trace sees only the steps")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the legs of the other workloads (the tiny "
+                         "prefill's latency, the long-context and the varlen "
+                         "prefill), taken after the timed steps")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB per "
                          "step (reference kernel for HBM counter scaling)")
@@ -328,6 +349,12 @@ def main(argv=None):
     epi = None
     if args.epilogue and not args.step_only:
         epi = time_epilogue(po, dq, dk, dv, dg, dbeta, states, dev, stream, ev)
+    legs, samples = None, {}
+    if not args.step_only and not args.no_workloads:
+        legs = {"tiny": time_tiny(dev, stream, ev)}
+        for name in ("long", "varlen"):
+            legs[name], samples[name] = time_prefill_workload(
+                name, dev, stream, ev)
 
     # ---------------- derived figures --------------------------------------
     D, H = dp.K, dp.H
@@ -343,18 +370,6 @@ def main(argv=None):
     elt = pq.element_size()
     prep_b = counts.prep_bytes(total * pp.H, chunks, pp.C, pp.K, pp.V, elt)
     recur_b = counts.recur_bytes(total * pp.H, chunks, pp.C, pp.K, pp.V, elt)
-
-    def kernel_entry(name, src_file, nbytes, ms):
-        avg, med = float(np.mean(ms)), float(np.median(ms))
-        ach = nbytes / (avg * 1e-3) / 1e9
-        return {"kernel": name, "bound": "hbm", "achieved": round(ach, 2),
-                "peak": counts.HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(ach / counts.HBM_PEAK_GBPS, 4),
-                "traffic": read_traffic(src_file),
-                "algorithmic_bytes_per_launch": nbytes,
-                "avg_launch_ms": round(avg, 5),
-                "median_launch_ms": round(med, 5),
-                "mfma": mfma_figures(src_file, avg)}
 
     kernels = []
     if prep_ms is not None:
@@ -442,12 +457,137 @@ def main(argv=None):
     if pro is not None:
         pro["plain_prefill_ms"] = round(pre_avg, 5)
         result["prologue"] = pro
+    if legs is not None:
+        result["workloads"] = legs
 
     # ---------------- CPU baseline: the oracle on the host cores -----------
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(dp, pp)
+        result["cpu_baseline"] = cpu_baseline(dp, pp, samples)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def time_tiny(dev, stream, ev):
+    """The tiny fp32 prefill (B=1, H=2, T=64, d=16, C=16) as one
+    kda_prefill_chunked call: its device time back to back, and the host's
+    latency from the call to its completion."""
+    import torch
+    from linear_recurrent_attention_kda_amd import kda
+    p = inputs.make("tiny", seed=0)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa
+    q, k, v, g, beta = (t(x) for x in (p.q, p.k, p.v, p.g, p.beta))
+    o = torch.empty((p.B, p.T, p.H, p.V), dtype=torch.float32, device=dev)
+    fs = torch.empty((p.B, p.H, p.K, p.V), dtype=torch.float32, device=dev)
+    ws = kda.workspace_for(p.B, p.B * p.T, p.H, p.K, p.V, p.C, dev)
+    run = lambda: kda.kda_prefill_chunked(  # noqa: E731
+        q, k, v, g, beta, None, chunk_size=p.C, final_state=fs, o=o,
+        workspace=ws)
+    for _ in range(10):
+        run()
+    torch.cuda.synchronize()
+    n = 200
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for _ in range(n):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dev_us = e0.elapsed_time(e1) / n * 1e3
+    lat = []
+    for _ in range(50):
+        t0 = time.perf_counter()
+        run()
+        torch.cuda.synchronize()
+        lat.append((time.perf_counter() - t0) * 1e6)
+    log("tiny prefill: %.2f us per call back to back, %.1f us call to "
+        "completion (median)" % (dev_us, float(np.median(lat))))
+    return {"workload": "tiny: B=1, H=2, T=64, d=16, C=16, fp32, zero state",
+            "device_us_back_to_back": round(dev_us, 3),
+            "latency_us_median": round(float(np.median(lat)), 2),
+            "latency_us_min": round(float(np.min(lat)), 2),
+            "launches": 2, "tokens": p.B * p.T}
+
+
+def time_prefill_workload(name, dev, stream, ev, reps=5):
+    """One prefill workload (inputs drawn on the device, same recipe as the
+    tests' host draws), run as its two stages so that each kernel is timed
+    on its own: `reps` launches of each, between events, after two warm-up
+    calls.  Returns the leg's figures and a host copy of a head sample for
+    the oracle's timing."""
+    import torch
+    from linear_recurrent_attention_kda_amd import kda
+    t_gen = time.time()
+    w = inputs.make_device(name, seed=0, device=dev)
+    total, H, K, V, C = w["total"], w["H"], w["K"], w["V"], w["C"]
+    nseq = len(w["lengths"])
+    maxlen = int(w["lengths"].max())
+    cu = w["cu_seqlens"]
+    o = torch.empty((total, H, V), dtype=w["q"].dtype, device=dev)
+    fs = torch.empty((nseq, H, K, V), dtype=torch.float32, device=dev)
+    ws = kda.workspace_for(nseq, total, H, K, V, C, dev)
+    torch.cuda.synchronize()
+    log("%s inputs drawn on the device in %.1fs" % (name, time.time() - t_gen))
+
+    def prep():
+        kda.kda_prefill_varlen_prep(w["q"], w["k"], w["v"], w["g"], w["beta"],
+                                    cu, maxlen, chunk_size=C, workspace=ws)
+
+    def recur():
+        kda.kda_prefill_varlen_recur(ws, cu, maxlen, total, H, K, V,
+                                     w["q"].dtype, w["initial_state"],
+                                     chunk_size=C, final_state=fs, o=o)
+    for _ in range(2):
+        prep()
+        recur()
+    prep_ms, recur_ms = [], []
+    for _ in range(reps):
+        a, m, b = ev(), ev(), ev()
+        a.record(stream)
+        prep()
+        m.record(stream)
+        recur()
+        b.record(stream)
+        torch.cuda.synchronize()
+        prep_ms.append(a.elapsed_time(m))
+        recur_ms.append(m.elapsed_time(b))
+    tot_ms = float(np.mean(prep_ms)) + float(np.mean(recur_ms))
+    chunks = int(np.sum((w["lengths"] + C - 1) // C)) * H
+    elt = w["q"].element_size()
+    flops = counts.prefill_flops_per_chunk(C, K) * chunks
+    log("%s prefill: prep %.4f ms, recurrence %.4f ms"
+        % (name, float(np.mean(prep_ms)), float(np.mean(recur_ms))))
+    leg = {
+        "workload": "%s: %d sequence(s), %d tokens, H=%d, d=%d, C=%d, %s, "
+                    "%s initial state" % (name, nseq, total, H, K, C,
+                                          w["dtype"], "zero"
+                                          if w["initial_state"] is None
+                                          else "nonzero"),
+        "sequence_lengths": [int(x) for x in w["lengths"]],
+        "ms": round(tot_ms, 4),
+        "tokens_per_s": round(total / (tot_ms * 1e-3), 1),
+        "pages_flops": flops,
+        "mfma_util_frac": round(flops / (tot_ms * 1e-3) / 1e12 /
+                                counts.BF16_MFMA_PEAK_TFLOPS, 4),
+        "kernels": [
+            kernel_entry("prep_kernel (kda_prep.hip)", "kda_prep.hip",
+                         counts.prep_bytes(total * H, chunks, C, K, V, elt),
+                         prep_ms, traffic=False),
+            kernel_entry("chunk recurrence (kda_recur.hip)", "kda_recur.hip",
+                         counts.recur_bytes(total * H, chunks, C, K, V, elt),
+                         recur_ms, traffic=False)],
+    }
+    # a head sample for the oracle's timing: 16 heads, every token
+    nh = min(16, H)
+    host = lambda x: x[:, :nh].float().cpu().numpy()  # noqa: E731
+    sample = dict(q=host(w["q"]), k=host(w["k"]), v=host(w["v"]),
+                  g=host(w["g"]), beta=w["beta"][:, :nh].cpu().numpy(),
+                  s0=None if w["initial_state"] is None else
+                  w["initial_state"][:, :nh].cpu().numpy(),
+                  cu=w["cu_seqlens"].cpu().numpy(), heads=nh, H=H,
+                  total=total)
+    del w, o, fs, ws
+    torch.cuda.empty_cache()
+    return leg, sample
 
 
 def time_spec(T, dp, states, dev, stream, ev):
@@ -599,13 +739,23 @@ def time_epilogue(po, dq, dk, dv, dg, dbeta, states, dev, stream, ev):
     }
 
 
-def cpu_baseline(dp, pp):
+def host_cpus() -> int:
+    """CPUs this process may run on (its affinity mask), else the count."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(dp, pp, samples=None):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
-    workloads: the whole decode step, and one prefill head per thread over
-    all of the prefill's tokens (scaled to all heads)."""
+    workloads: the whole decode step, the prefill over a head sample of all
+    of its tokens (scaled to all heads), and the same for the other
+    workloads' legs.  Threads: every CPU the process may use, capped at 16,
+    the host-CPU share of one GPU on the machines this runs on."""
     import oracle
     oracle.build(force=False)
-    threads = min(16, os.cpu_count() or 1)
+    threads = max(1, min(16, host_cpus()))
     oracle.set_threads(threads)
     # each leg repeats (same inputs, results discarded) until it has run
     # for a few seconds, so that the rate is not one short noisy sample
@@ -637,10 +787,36 @@ def cpu_baseline(dp, pp):
     pre_tps = total / (pre_s * pp.H / len(heads))
     log("oracle: decode %.3fs x %d, prefill sample %.3fs x %d"
         % (dec_s, dec_reps, pre_s, pre_reps))
+    legs = {}
+    for name, smp in (samples or {}).items():
+        reps, t = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t < 2.0:
+            oracle.run_varlen(smp["q"], smp["k"], smp["v"], smp["g"],
+                              smp["beta"], smp["cu"], smp["s0"])
+            reps += 1
+        sec = (time.perf_counter() - t) / reps
+        legs[name] = {
+            "tokens_per_s": round(smp["total"] / (sec * smp["H"] /
+                                                  smp["heads"]), 1),
+            "sample": "%d of %d heads over all %d tokens, scaled to all "
+                      "heads, mean of %d runs" % (smp["heads"], smp["H"],
+                                                   smp["total"], reps),
+            "sample_seconds": round(sec, 4)}
+        log("oracle: %s sample %.3fs x %d" % (name, sec, reps))
+    tiny = inputs.make("tiny", seed=0)
+    reps, t = 0, time.perf_counter()
+    while reps == 0 or time.perf_counter() - t < 0.5:
+        oracle.run_fixed(tiny.q, tiny.k, tiny.v, tiny.g, tiny.beta)
+        reps += 1
+    legs["tiny"] = {"seconds_per_call": round((time.perf_counter() - t) /
+                                              reps, 7), "runs": reps}
     return {
         "value": round(dec_bytes / dec_s / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
+        "threads": threads,
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": host_cpus(),
         "kind": "oracle",
         "sample": "whole decode step (%dx%d heads, d=%d) in fp64, mean of "
                   "%d runs; prefill: %d of %d heads over all %d tokens, "
@@ -648,6 +824,7 @@ def cpu_baseline(dp, pp):
                   % (dp.B, dp.H, dp.K, dec_reps, len(heads), pp.H, total,
                      pre_reps),
         "prefill_tokens_per_s": round(pre_tps, 1),
+        "workloads": legs,
         "decode_seconds": round(dec_s, 4),
         "prefill_sample_seconds": round(pre_s, 4),
         "cpu_model": cpu_model(),

@@ -18,6 +18,11 @@ lengths, q, k, v, g, beta, initial state; all draws in float32):
   beta  = sigmoid(N(0, 1)) per (token, head), fp32
   S0    ~ N(0, 0.02^2) (std 0.02), fp32, or absent (zero state)
 bf16 rounding is round-to-nearest-even on the float32 bit pattern.
+
+`make_device` draws the same recipe directly on the GPU with torch's seeded
+generator (a different random stream, the same distributions, shapes and
+sequence lengths): the benchmark uses it for its largest workloads, whose
+host-side draws take about a minute each.
 """
 from __future__ import annotations
 
@@ -158,3 +163,54 @@ def make(name: str, seed: int = 0, **overrides) -> Problem:
                    initial_state=s0, cu_seqlens=cu,
                    B=cfg.get("B", 0), T=cfg.get("T", 0),
                    N=nseq if kind == "varlen" else 0)
+
+
+def varlen_lengths(name: str, seed: int = 0, **overrides) -> np.ndarray:
+    """The sequence lengths `make` draws for a varlen workload (its first
+    draw from the seeded generator)."""
+    cfg = dict(WORKLOADS[name])
+    cfg.update(overrides)
+    if "lengths" in cfg:
+        return np.asarray(cfg["lengths"], np.int64)
+    rng = np.random.default_rng(seed)
+    return rng.integers(cfg["len_lo"], cfg["len_hi"] + 1, size=cfg["N"])
+
+
+def make_device(name: str, seed: int, device, **overrides) -> dict:
+    """Workload ``name`` drawn on ``device`` with torch (recipe as `make`).
+    Returns a dict of device tensors q, k, v, g, beta, initial_state (or
+    None) and cu_seqlens (int32, also for fixed-length workloads: B
+    sequences of T tokens), plus the sizes."""
+    import torch
+    cfg = dict(WORKLOADS[name])
+    cfg.update(overrides)
+    kind = cfg["kind"]
+    if kind == "decode":
+        raise ValueError("make_device covers the prefill workloads")
+    H, K, V = cfg["H"], cfg["K"], cfg["V"]
+    if kind == "varlen":
+        lengths = varlen_lengths(name, seed, **overrides)
+    else:
+        lengths = np.full(cfg["B"], cfg["T"], np.int64)
+    cu = np.zeros(len(lengths) + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    total = int(cu[-1])
+    gen = torch.Generator(device=device).manual_seed(int(seed))
+    dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+
+    def normal(*shape):
+        return torch.randn(shape, generator=gen, device=device,
+                           dtype=torch.float32)
+
+    def unit(x):
+        return x / torch.sqrt(torch.sum(x * x, dim=-1, keepdim=True))
+
+    q = unit(normal(total, H, K)).to(dt)
+    k = unit(normal(total, H, K)).to(dt)
+    v = normal(total, H, V).to(dt)
+    g = -5.0 * torch.sigmoid(normal(total, H, K) + float(cfg["g_mu"]))
+    beta = torch.sigmoid(normal(total, H))
+    s0 = 0.02 * normal(len(lengths), H, K, V) if cfg["s0"] else None
+    return dict(name=name, q=q, k=k, v=v, g=g, beta=beta, initial_state=s0,
+                cu_seqlens=torch.from_numpy(cu).to(device), lengths=lengths,
+                H=H, K=K, V=V, C=cfg["C"], dtype=cfg["dtype"], total=total)
