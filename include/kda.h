@@ -66,8 +66,12 @@ typedef enum kda_status {
   KDA_ERR_INVALID_ARG = -1, /* NULL / misaligned pointer, bad size or count */
   KDA_ERR_UNSUPPORTED = -2, /* head dims, chunk size or dtype not built     */
   KDA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required   */
-  KDA_ERR_LAUNCH = -4       /* a kernel launch failed                        */
+  KDA_ERR_LAUNCH = -4,      /* a kernel launch failed                        */
+  KDA_ERR_SCRATCH = -5      /* needs more than KDA_NOALLOC_SCRATCH_BYTES     */
 } kda_status_t;
+
+/* Size of the fixed device scratch buffer of kda_prefill_varlen_noalloc. */
+#define KDA_NOALLOC_SCRATCH_BYTES (256u << 20)
 
 typedef enum kda_dtype {
   KDA_DTYPE_BF16 = 0, /* q, k, v, o in bfloat16 */
@@ -148,6 +152,34 @@ kda_status_t kda_prefill_varlen(const void* q, const void* k, const void* v,
                                 int32_t Dk, int32_t Dv, int32_t C, float scale,
                                 int32_t dtype, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * kda_prefill_varlen for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace: the prefill workspace lives in a fixed
+ * device array of KDA_NOALLOC_SCRATCH_BYTES (256 MiB) inside the library,
+ * which each GPU it runs on holds from the first call on that device until
+ * the process ends.  The call itself allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); its first call on a device looks
+ * up that device's copy of the array once.
+ *   Limit: kda_prefill_workspace_size(N, total_T, H, Dk, Dv, C) must not
+ *   exceed KDA_NOALLOC_SCRATCH_BYTES (about 3,600 chunk-heads at Dk = Dv =
+ *   128, C = 64, e.g. 96 heads x 2,300 tokens), else KDA_ERR_SCRATCH and
+ *   nothing is enqueued.
+ *   Concurrency: every call on one GPU uses the same array, so calls that
+ *   overlap on one GPU (different streams, or host threads) race and must
+ *   be serialised by the caller; calls on different GPUs are independent.
+ *   The array keeps the last call's contents; no part of it needs to start
+ *   at zero (every workspace byte a call reads is written earlier in the
+ *   same call).
+ * Arguments, results and every other error as kda_prefill_varlen.
+ */
+kda_status_t kda_prefill_varlen_noalloc(
+    const void* q, const void* k, const void* v, const float* g,
+    const float* beta, const int32_t* cu_seqlens, int32_t N, int64_t total_T,
+    int32_t max_seqlen, const float* initial_state, float* final_state,
+    void* o, int32_t H, int32_t Dk, int32_t Dv, int32_t C, float scale,
+    int32_t dtype, void* stream);
 
 /*
  * The two stages of kda_prefill_varlen, for callers that schedule them

@@ -6,9 +6,41 @@
 
 #include <limits.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "kda_internal.hpp"
 
+// Prefill workspace of kda_prefill_varlen_noalloc: a fixed device array that
+// each GPU the library runs on holds until the process ends.  In host code
+// this name is only a stand-in for the array: its device address comes from
+// hipGetSymbolAddress (scratch_ptr below), never from the name itself.
+static __device__ __align__(256) char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Device address of `scratch` on the current device, fetched once per device
+// (each GPU holds its own copy at its own address).  nullptr on failure.
+void* scratch_ptr() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(mu);
+  p = addr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q)
+      return nullptr;
+    addr[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
 
 bool aligned(const void* p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) % a) == 0;
@@ -35,17 +67,21 @@ kda_status_t check_prefill_common(int32_t H, int32_t Dk, int32_t Dv,
 // the chunk-recurrence kernel (reads it).
 constexpr int kStagePrep = 1, kStageRecur = 2, kStagesBoth = 3;
 
+// With validate_only, every check except the workspace's runs and nothing is
+// launched.
 kda_status_t run_prefill(kda::PrefillArgs& a, int32_t D, int32_t C,
                          int32_t dtype, void* workspace,
                          size_t workspace_bytes, void* stream,
-                         int stages = kStagesBoth) {
+                         int stages = kStagesBoth,
+                         bool validate_only = false) {
   const size_t need = kda_prefill_workspace_size(a.N, a.total_T, a.H, D, D, C);
   if (need == 0) return KDA_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
-  if (!aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
   // the prep kernel indexes its (sequence, chunk, head) items in 32 bits
   if ((int64_t)a.N * a.max_chunks * a.H >= ((int64_t)1 << 31))
     return KDA_ERR_UNSUPPORTED;
+  if (validate_only) return KDA_OK;
+  if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
   a.ws = static_cast<char*>(workspace);
   a.nslots = kda::num_slots(a.N, a.total_T, C);
   const bool bf16_io = dtype == KDA_DTYPE_BF16;
@@ -129,7 +165,8 @@ kda_status_t prefill_varlen(const void* q, const void* k, const void* v,
                             int32_t C, float scale, int32_t dtype,
                             const CkptOpts& ck, const float* conv_w,
                             void* workspace, size_t workspace_bytes,
-                            void* stream, int stages = kStagesBoth) {
+                            void* stream, int stages = kStagesBoth,
+                            bool validate_only = false) {
   if (N <= 0 || total_T < 0 || max_seqlen < 0) return KDA_ERR_INVALID_ARG;
   if (total_T > 0 && max_seqlen == 0) return KDA_ERR_INVALID_ARG;
   kda_status_t st = check_prefill_common(H, Dk, Dv, C, dtype);
@@ -167,7 +204,7 @@ kda_status_t prefill_varlen(const void* q, const void* k, const void* v,
   a.scale = scale;
   a.conv_w = conv_w;
   return run_prefill(a, Dk, C, dtype, workspace, workspace_bytes, stream,
-                     stages);
+                     stages, validate_only);
 }
 
 kda_status_t decode_step(const void* q, const void* k, const void* v,
@@ -213,6 +250,8 @@ const char* kda_status_string(int32_t status) {
     case KDA_ERR_UNSUPPORTED: return "unsupported size, chunk or dtype";
     case KDA_ERR_WORKSPACE: return "workspace missing or too small";
     case KDA_ERR_LAUNCH: return "kernel launch failed";
+    case KDA_ERR_SCRATCH:
+      return "problem needs more workspace than the fixed scratch buffer";
   }
   return "unknown status";
 }
@@ -275,6 +314,31 @@ kda_status_t kda_prefill_varlen(const void* q, const void* k, const void* v,
                         initial_state, final_state, o, H, Dk, Dv, C, scale,
                         dtype, CkptOpts{}, nullptr, workspace,
                         workspace_bytes, stream);
+}
+
+kda_status_t kda_prefill_varlen_noalloc(
+    const void* q, const void* k, const void* v, const float* g,
+    const float* beta, const int32_t* cu_seqlens, int32_t N, int64_t total_T,
+    int32_t max_seqlen, const float* initial_state, float* final_state,
+    void* o, int32_t H, int32_t Dk, int32_t Dv, int32_t C, float scale,
+    int32_t dtype, void* stream) {
+  const size_t need = kda_prefill_workspace_size(N, total_T, H, Dk, Dv, C);
+  void* ws = nullptr;
+  if (need > 0) {  // (need == 0: invalid sizes, reported below)
+    if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH;
+    // every other check runs before the first HIP call
+    const kda_status_t st = prefill_varlen(
+        q, k, v, g, beta, cu_seqlens, N, total_T, max_seqlen, initial_state,
+        final_state, o, H, Dk, Dv, C, scale, dtype, CkptOpts{}, nullptr,
+        nullptr, 0, stream, kStagesBoth, /*validate_only=*/true);
+    if (st != KDA_OK) return st;
+    ws = scratch_ptr();
+    if (!ws) return KDA_ERR_LAUNCH;
+  }
+  return prefill_varlen(q, k, v, g, beta, cu_seqlens, N, total_T, max_seqlen,
+                        initial_state, final_state, o, H, Dk, Dv, C, scale,
+                        dtype, CkptOpts{}, nullptr, ws,
+                        (size_t)KDA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 kda_status_t kda_prefill_varlen_prep(const void* q, const void* k,

@@ -21,6 +21,8 @@ LIB_PATH = os.environ.get("KDA_LIB", os.path.join(_PKG, "libkda.so"))
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "kda.h")
 
 KDA_OK = 0
+KDA_ERR_SCRATCH = -5
+KDA_NOALLOC_SCRATCH_BYTES = 256 << 20
 KDA_DTYPE_BF16 = 0
 KDA_DTYPE_FP32 = 1
 
@@ -63,6 +65,10 @@ def load() -> ctypes.CDLL:
         lib.kda_prefill_varlen.argtypes = [
             vp, vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, i32,
             i32, f32, i32, vp, sz, vp]
+        lib.kda_prefill_varlen_noalloc.restype = i32
+        lib.kda_prefill_varlen_noalloc.argtypes = [
+            vp, vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, i32,
+            i32, f32, i32, vp]
         lib.kda_prefill_varlen_prep.restype = i32
         lib.kda_prefill_varlen_prep.argtypes = [
             vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, i32,
@@ -308,6 +314,42 @@ def kda_prefill_varlen_recur(workspace, cu_seqlens, max_seqlen: int,
         _dtype_code(o), _ptr(workspace), workspace.numel(), _stream(dev))
     if st != KDA_OK:
         raise KDAError("kda_prefill_varlen_recur", st)
+    return o, final_state
+
+
+def kda_prefill_varlen_noalloc(q, k, v, g, beta, cu_seqlens,
+                               max_seqlen: int, initial_state=None, *,
+                               chunk_size: int = 64, scale: float = 1.0,
+                               final_state=None, o=None):
+    """kda_prefill_varlen with the workspace in the library's fixed device
+    scratch array (no workspace argument; the library call allocates
+    nothing).  final_state and o must be passed in (this wrapper allocates
+    nothing either).  Calls that overlap on one GPU race on the scratch
+    array.  Returns (o, final_state)."""
+    lib = load()
+    total_T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    N = cu_seqlens.numel() - 1
+    for t, n, s, dt in ((q, "q", (total_T, H, Dk), q.dtype),
+                        (k, "k", (total_T, H, Dk), q.dtype),
+                        (v, "v", (total_T, H, Dv), q.dtype),
+                        (g, "g", (total_T, H, Dk), torch.float32),
+                        (beta, "beta", (total_T, H), torch.float32),
+                        (cu_seqlens, "cu_seqlens", (N + 1,), torch.int32),
+                        (o, "o", (total_T, H, Dv), q.dtype)):
+        _check(t, n, s, dt, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (N, H, Dk, Dv), torch.float32,
+               dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (N, H, Dk, Dv), torch.float32, dev)
+    st = lib.kda_prefill_varlen_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N,
+        total_T, int(max_seqlen), _ptr(initial_state), _ptr(final_state),
+        _ptr(o), H, Dk, Dv, chunk_size, scale, _dtype_code(q), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_prefill_varlen_noalloc", st)
     return o, final_state
 
 

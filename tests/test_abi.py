@@ -34,6 +34,7 @@ def test_exports_every_declared_symbol():
                           "kda_prefill_workspace_size", "kda_prefill_chunked",
                           "kda_prefill_varlen", "kda_prefill_varlen_ckpt",
                           "kda_prefill_varlen_ckpt_at",
+                          "kda_prefill_varlen_noalloc",
                           "kda_decode_step", "kda_spec_verify",
                           "kda_spec_commit", "kda_output_norm_gate",
                           "kda_decode_step_gated",
@@ -47,7 +48,7 @@ def test_exports_every_declared_symbol():
 def test_version_and_status_strings():
     assert kda.kda_abi_version() == 1
     assert kda.kda_status_string(0) == "ok"
-    for s in (-1, -2, -3, -4):
+    for s in (-1, -2, -3, -4, -5):
         assert kda.kda_status_string(s) not in ("ok", "unknown status")
     assert kda.kda_status_string(7) == "unknown status"
 
@@ -138,6 +139,35 @@ def test_prefill_varlen_validation():
     assert _varlen(lib, C=8) == UNSUP
     assert _varlen(lib, ws_bytes=10) == WS
     assert _varlen(lib, v=NULL) == INVALID
+
+
+def _noalloc(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, cu=P, N=2, total=100, maxlen=64,
+             s0=NULL, s1=NULL, o=P, H=2, Dk=64, Dv=64, C=64, scale=1.0,
+             dtype=0, stream=NULL)
+    a.update(kw)
+    return lib.kda_prefill_varlen_noalloc(
+        a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"],
+        a["total"], a["maxlen"], a["s0"], a["s1"], a["o"], a["H"], a["Dk"],
+        a["Dv"], a["C"], a["scale"], a["dtype"], a["stream"])
+
+
+def test_prefill_varlen_noalloc_validation():
+    """Argument errors as kda_prefill_varlen, and a problem whose workspace
+    exceeds the fixed scratch array is refused before any HIP call."""
+    lib = kda.load()
+    assert _noalloc(lib, N=0) == INVALID
+    assert _noalloc(lib, cu=NULL) == INVALID
+    assert _noalloc(lib, maxlen=0) == INVALID
+    assert _noalloc(lib, C=8) == UNSUP
+    assert _noalloc(lib, Dk=256, Dv=256) == UNSUP
+    assert _noalloc(lib, q=NULL) == INVALID
+    assert _noalloc(lib, s1=MIS) == INVALID
+    # 96 heads x 8192 tokens at d = 128: 912 MB of workspace > 256 MiB
+    assert kda.kda_prefill_workspace_size(1, 8192, 96, 128, 128, 64) > \
+        kda.KDA_NOALLOC_SCRATCH_BYTES
+    assert _noalloc(lib, N=1, total=8192, maxlen=8192, H=96, Dk=128,
+                    Dv=128) == -5
 
 
 def _prep(lib, **kw):
