@@ -153,10 +153,11 @@ def main(argv=None):
                     help="also time speculative verify + commit of this many "
                          "draft tokens per sequence on the decode batch "
                          "(outside the timed steps)")
-    ap.add_argument("--epilogue", action="store_true",
-                    help="also time the output epilogue: standalone over the "
-                         "prefill output, and fused into the decode step "
-                         "(outside the timed steps)")
+    ap.add_argument("--no-epilogue", action="store_true",
+                    help="skip timing the output epilogue (standalone over "
+                         "the prefill output, fused into the prefill's "
+                         "recurrence, fused into the decode step), taken "
+                         "after the timed steps")
     ap.add_argument("--prologue", action="store_true",
                     help="also time the prefill with the input prologue "
                          "fused (outside the timed steps)")
@@ -347,8 +348,11 @@ def main(argv=None):
     if args.prologue and not args.step_only:
         pro = time_prologue(pp, nseq, total, ws, dev, stream, ev)
     epi = None
-    if args.epilogue and not args.step_only:
+    if not args.no_epilogue and not args.step_only:
         epi = time_epilogue(po, dq, dk, dv, dg, dbeta, states, dev, stream, ev)
+        epi["prefill_gated"] = time_gated_prefill(
+            (pq_, pk_, pv_, pg_, pbeta_), cu, maxlen, total, pp.H, pp.K,
+            pp.V, pp.C, ps0, ws, dev, stream, ev)
     legs, samples = None, {}
     if not args.step_only and not args.no_workloads:
         legs = {"tiny": time_tiny(dev, stream, ev)}
@@ -576,6 +580,9 @@ def time_prefill_workload(name, dev, stream, ev, reps=5):
                          counts.recur_bytes(total * H, chunks, C, K, V, elt),
                          recur_ms, traffic=False)],
     }
+    leg["gated"] = time_gated_prefill(
+        (w["q"], w["k"], w["v"], w["g"], w["beta"]), cu, maxlen, total, H, K,
+        V, C, w["initial_state"], ws, dev, stream, ev, n=3)
     # a head sample for the oracle's timing: 16 heads, every token
     nh = min(16, H)
     host = lambda x: x[:, :nh].float().cpu().numpy()  # noqa: E731
@@ -686,6 +693,54 @@ def time_prologue(pp, nseq, total, ws, dev, stream, ev):
     log("prologue-fused prefill: %.4f ms" % ms)
     return {"fused_prefill_ms": round(ms, 5),
             "tokens_per_s": round(total / (ms * 1e-3), 1)}
+
+
+def time_gated_prefill(ins, cu, maxlen, total, H, K, V, C, s0, ws, dev,
+                       stream, ev, n=5):
+    """kda_prefill_varlen_gated (the output epilogue fused into the
+    recurrence when there are at least two (sequence, head) pairs per
+    compute unit, else the plain recurrence then the epilogue kernel),
+    against the plain prefill followed by kda_output_norm_gate; each n
+    launches back to back between two events."""
+    import torch
+    from linear_recurrent_attention_kda_amd import kda
+    q, k, v, g, beta = ins
+    nseq = len(cu) - 1
+    gen = torch.Generator(device=dev).manual_seed(6)
+    z = torch.randn((total, H, V), generator=gen, device=dev).to(q.dtype)
+    w = 1.0 + 0.3 * torch.randn(V, generator=gen, device=dev)
+    y = torch.empty_like(z)
+    o = torch.empty_like(z)
+    fs = torch.empty((nseq, H, K, V), dtype=torch.float32, device=dev)
+
+    def gated():
+        kda.kda_prefill_varlen_gated(q, k, v, g, beta, cu, maxlen, s0, z=z,
+                                     w=w, chunk_size=C, final_state=fs, y=y,
+                                     workspace=ws)
+
+    def two_pass():
+        kda.kda_prefill_varlen(q, k, v, g, beta, cu, maxlen, s0,
+                               chunk_size=C, final_state=fs, o=o,
+                               workspace=ws)
+        kda.kda_output_norm_gate(o, z, w, y=y)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    t_g, t_2 = timed(gated), timed(two_pass)
+    path = "fused" if nseq * H >= 2 * cus else "two-pass"
+    log("gated prefill (%s): %.4f ms; plain + epilogue %.4f ms"
+        % (path, t_g, t_2))
+    return {"gated_ms": round(t_g, 5), "gated_path": path,
+            "plain_then_epilogue_ms": round(t_2, 5)}
 
 
 def time_epilogue(po, dq, dk, dv, dg, dbeta, states, dev, stream, ev):

@@ -86,10 +86,9 @@ const char* kda_status_string(int32_t status);
 
 /*
  * Bytes of device workspace that the prefill entry points (kda_prefill_chunked,
- * kda_prefill_varlen and its _ckpt, _ckpt_at, _prologue, _prep and _recur
- * forms) need
- * for N sequences holding total_T tokens (fixed length: N = B,
- * total_T = B*T).  The workspace holds, per head and chunk, the chunk-prep
+ * kda_prefill_varlen and its _ckpt, _ckpt_at, _gated, _prologue, _prep and
+ * _recur forms; _noalloc holds it internally) need for N sequences holding
+ * total_T tokens (fixed length: N = B, total_T = B*T).  The workspace holds, per head and chunk, the chunk-prep
  * kernel's outputs that the chunk-recurrence kernel consumes ("FlashKDA
  * algorithm": K1 prepares chunk tensors in parallel, K2 runs the chunk-level
  * recurrence).  Returns 0 for unsupported sizes.
@@ -152,6 +151,34 @@ kda_status_t kda_prefill_varlen(const void* q, const void* k, const void* v,
                                 int32_t Dk, int32_t Dv, int32_t C, float scale,
                                 int32_t dtype, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * kda_prefill_varlen with the block's output epilogue fused into the
+ * chunk-recurrence kernel ("Kimi K3: The Manos, The Mythos, The Legendos",
+ * section "Kimi Linear": the operator's output is normalised per head and
+ * scaled by an output gate before the heads are mixed).  The outputs o never
+ * reach memory; per (token, head) row of Dv channels the kernel writes
+ *   y = o * rsqrt(mean(o^2) + eps) * w * sigmoid(z)
+ * as kda_output_norm_gate would on o.  The fused recurrence holds whole
+ * rows, one workgroup per (sequence, head) instead of one per d_v slice, so
+ * it is used when N * H is at least twice the device's compute units (with
+ * fewer pairs the d_v slices' parallelism is worth more than the saved pass
+ * over o).  Below that the plain recurrence writes o into y and the
+ * epilogue kernel then rewrites y in place, bit for bit
+ * kda_prefill_varlen followed by kda_output_norm_gate.
+ *   z     [total_T, H, Dv] dtype, the gate's pre-activation
+ *   w     [Dv] fp32, per-channel weight shared by the heads;  eps >= 0
+ *   y     [total_T, H, Dv] dtype, written in place of o
+ * z and w may be NULL only when total_T == 0.  All other arguments, and
+ * every error, as kda_prefill_varlen.
+ */
+kda_status_t kda_prefill_varlen_gated(
+    const void* q, const void* k, const void* v, const float* g,
+    const float* beta, const int32_t* cu_seqlens, int32_t N, int64_t total_T,
+    int32_t max_seqlen, const float* initial_state, float* final_state,
+    const void* z, const float* w, float eps, void* y, int32_t H, int32_t Dk,
+    int32_t Dv, int32_t C, float scale, int32_t dtype, void* workspace,
+    size_t workspace_bytes, void* stream);
 
 /*
  * kda_prefill_varlen for callers that cannot allocate device memory: code

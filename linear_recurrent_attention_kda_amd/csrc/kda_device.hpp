@@ -192,6 +192,20 @@ __device__ __forceinline__ void buffer_store4(float*, __amdgpu_buffer_rsrc_t r,
                                          0, 0);
 }
 
+// Four storage-dtype elements at byte offset `off` of buffer r, as floats
+// (out of range: zeros).  The pointer argument only selects the dtype.
+__device__ __forceinline__ f32x4 load4(const bf16*, __amdgpu_buffer_rsrc_t r,
+                                       uint32_t off) {
+  const bf16x4 v = __builtin_bit_cast(
+      bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4 load4(const float*, __amdgpu_buffer_rsrc_t r,
+                                       uint32_t off) {
+  return __builtin_bit_cast(f32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // Four consecutive storage-dtype elements (8-byte aligned for bf16, 16-byte
 // for fp32) from x * scale.
 __device__ __forceinline__ void store4(bf16* p, f32x4 x, float scale) {

@@ -96,6 +96,13 @@ struct PrefillArgs {
   // pre-activation a (g = -5 sigmoid(a)) and beta the pre-activation b
   // (beta = sigmoid(b)); conv_w is [3, H, D, 4] fp32 (taps of q, k, v).
   const float* conv_w;
+  // Output epilogue fused into the recurrence when gate_z != nullptr: the
+  // outputs are written as y = o * rsqrt(mean(o^2) + gate_eps) * gate_w *
+  // sigmoid(gate_z) per (token, head) row; gate_z [total_T, H, Dv] in the
+  // storage dtype, gate_w [Dv] fp32.
+  const void* gate_z;
+  const float* gate_w;
+  float gate_eps;
 };
 
 struct SpecArgs {
@@ -135,6 +142,9 @@ inline hipError_t launch_kernel(Kern kernel, dim3 grid, dim3 block,
   return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block,
                          args, 0, s);
 }
+
+// Compute units of the current device (queried once per device).
+int device_cus();
 
 // Return hipSuccess or the launch error.
 hipError_t launch_decode(const DecodeArgs& a, int D, bool bf16_io,

@@ -55,7 +55,8 @@ __device__ __forceinline__ unsigned xcd_logical_id(unsigned b, unsigned total,
   return (x + 8u * (k / nvt)) * nvt + k % nvt;
 }
 
-template <typename Tout, int D, int C, int BV, int PF, int NW, bool kCkpt>
+template <typename Tout, int D, int C, int BV, int PF, int NW, bool kCkpt,
+          bool kGated>
 __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
   constexpr int K = D, V = D;
   constexpr int NVT = V / BV;              // d_v slices per head
@@ -71,10 +72,14 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
   constexpr int SP = K + 8, UP = C + 8;    // padded LDS strides (bf16)
   static_assert(V % BV == 0 && BV % 16 == 0, "slice width");
   static_assert(UPW <= JT && (SPW % JT == 0 || SPW < JT), "wave tiling");
+  static_assert(!kGated || BV == V, "the fused epilogue needs whole rows");
   using Ops = ChunkOps<KSTEPS, CSTEPS, UPW, NCT>;
 
   __shared__ __attribute__((aligned(16))) bf16 s_SbT[BV][SP];  // S^T, bf16
   __shared__ __attribute__((aligned(16))) bf16 s_UbT[BV][UP];  // U^T, bf16
+  // fused epilogue: per-wave row sums of squares, when a row's columns are
+  // spread over several waves
+  __shared__ float s_ss[kGated && UPW < JT ? NW : 1][16];
 
   const unsigned bid = xcd_logical_id(blockIdx.x, gridDim.x, NVT);
   const int vt = bid % NVT;
@@ -278,6 +283,26 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
       }
     }
 
+    // fused epilogue: the gate pre-activations and weights of this wave's
+    // outputs, issued before the products that finish them
+    f32x4 zg[kGated ? UPW : 1], wg[kGated ? UPW : 1];
+    if constexpr (kGated) {
+      const __amdgpu_buffer_rsrc_t zrsrc = make_rsrc(
+          static_cast<const Tout*>(a.gate_z) + (t0 * H + h) * (int64_t)V,
+          (uint32_t)(((int64_t)(L - 1) * H * V + V) * sizeof(Tout)));
+#pragma unroll
+      for (int i = 0; i < UPW; ++i) {
+        const int jt = (u0 + i) % JT;
+        const int r = 16 * mrow + rl;
+        zg[i] = load4(static_cast<const Tout*>(nullptr), zrsrc,
+                      (uint32_t)(((int64_t)r * H * V + 16 * jt + 4 * kg) *
+                                 sizeof(Tout)));
+        const float4 w4 = *reinterpret_cast<const float4*>(
+            a.gate_w + 16 * jt + 4 * kg);
+        wg[i] = f32x4{w4.x, w4.y, w4.z, w4.w};
+      }
+    }
+
     // O^T += U^T M^T; store O (rows >= L fall outside the buffer: dropped)
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
@@ -287,11 +312,61 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
         for (int cs = 0; cs < CSTEPS; ++cs)
           if (2 * cs <= mrow)  // M is zero right of that
             Ot[i] = mfma_bf16(ubf[jt][cs], op.m[cs], Ot[i]);
-        const int r = 16 * mrow + rl;
-        buffer_store4(o, orsrc,
-                      (uint32_t)(((int64_t)r * H * V + 16 * jt + 4 * kg) *
-                                 sizeof(Tout)),
-                      Ot[i], a.scale);
+        if constexpr (!kGated) {
+          const int r = 16 * mrow + rl;
+          buffer_store4(o, orsrc,
+                        (uint32_t)(((int64_t)r * H * V + 16 * jt + 4 * kg) *
+                                   sizeof(Tout)),
+                        Ot[i], a.scale);
+        }
+      }
+    }
+    if constexpr (kGated) {
+      // y = o rsqrt(mean(o^2) + eps) w sigmoid(z) per (token, head) row
+      // ("Kimi K3: The Manos, The Mythos, The Legendos", section "Kimi
+      // Linear": per-head output norm and output gate).  Lane (rl, kg)
+      // holds columns 16 jt + 4 kg .. + 3 of row 16 mrow + rl.
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < UPW; ++i) {
+        if (kAllU || u0 + i < NUT) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = Ot[i][e] * a.scale;
+            ss += x * x;
+          }
+        }
+      }
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      if constexpr (UPW < JT) {
+        // the row's other columns belong to the waves with the same row
+        // tile: add their partial sums through LDS
+        if (kg == 0) s_ss[wave][rl] = (kAllU || has_u) ? ss : 0.f;
+        __syncthreads();
+        ss = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2)
+          if (w2 * UPW < NUT && (w2 * UPW) / JT == mrow) ss += s_ss[w2][rl];
+      }
+      const float rn = rsqrtf(ss * (1.f / V) + a.gate_eps);
+#pragma unroll
+      for (int i = 0; i < UPW; ++i) {
+        if (kAllU || u0 + i < NUT) {
+          const int jt = (u0 + i) % JT;
+          const int r = 16 * mrow + rl;
+          f32x4 y;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float gate = __builtin_amdgcn_rcpf(
+                1.f + __builtin_amdgcn_exp2f(-zg[i][e] * kLog2e));
+            y[e] = Ot[i][e] * a.scale * rn * wg[i][e] * gate;
+          }
+          buffer_store4(o, orsrc,
+                        (uint32_t)(((int64_t)r * H * V + 16 * jt + 4 * kg) *
+                                   sizeof(Tout)),
+                        y, 1.f);
+        }
       }
     }
     load_m(op, nb);
@@ -688,25 +763,6 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
   }
 }
 
-// Compute units of the current device, queried once per device and cached
-// (the query is not repeated on every launch).
-inline int device_cus() {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cache[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-    return 256;
-  int cus = cache[dev].load(std::memory_order_relaxed);
-  if (cus <= 0) {
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
-                              dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    cache[dev].store(cus, std::memory_order_relaxed);
-  }
-  return cus;
-}
-
 // Slice width.  Wider slices re-read the per-chunk tensors fewer times and
 // do more matrix work per chunk loaded; narrower ones give more workgroups
 // when there are few (sequence, head) pairs.  Measured on MI355X: 96 heads
@@ -741,17 +797,30 @@ hipError_t launch_w(const PrefillArgs& a, hipStream_t st) {
                                dim3(blocks), dim3(320), st, a);
   } else {
     return a.ckpt_states
-               ? launch_kernel(recur_kernel<Tout, D, C, BV, 2, 4, true>,
+               ? launch_kernel(recur_kernel<Tout, D, C, BV, 2, 4, true, false>,
                                dim3(blocks), dim3(256), st, a)
-               : launch_kernel(recur_kernel<Tout, D, C, BV, 2, 4, false>,
+               : launch_kernel(recur_kernel<Tout, D, C, BV, 2, 4, false, false>,
                                dim3(blocks), dim3(256), st, a);
   }
+}
+
+// Output epilogue fused into the recurrence: the row norm needs every value
+// channel of a row in one workgroup, so the slice is all of d_v (one
+// workgroup per (sequence, head)).  At d = 128 the whole-row slice keeps one
+// operand set in flight (two would spill registers).
+template <typename Tout, int D, int C>
+hipError_t launch_gated(const PrefillArgs& a, hipStream_t st) {
+  const unsigned blocks = (unsigned)a.H * (unsigned)a.N;
+  constexpr int PF = D == 128 ? 1 : 2;
+  return launch_kernel(recur_kernel<Tout, D, C, D, PF, 4, false, true>,
+                       dim3(blocks), dim3(256), st, a);
 }
 
 // Only the slice widths pick_bv can return are instantiated: 64 or 16 at
 // D = 128 and 64, 32 or 16 at D = 32, 16 at D = 16.
 template <typename Tout, int D, int C>
 hipError_t launch(const PrefillArgs& a, hipStream_t st) {
+  if (a.gate_z) return launch_gated<Tout, D, C>(a, st);
   const int bv = pick_bv(D, (int64_t)a.N * a.H);
   if constexpr (D >= 64) {
     if (bv == 64) return launch_w<Tout, D, C, 64>(a, st);
@@ -783,6 +852,25 @@ hipError_t launch_dc(const PrefillArgs& a, int D, int C, hipStream_t st) {
 }
 
 }  // namespace
+
+// Compute units of the current device, queried once per device and cached
+// (the query is not repeated on every launch).
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return 256;
+  int cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                              dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
 
 hipError_t launch_recur(const PrefillArgs& a, int D, int C, bool bf16_io,
                         hipStream_t st) {

@@ -65,6 +65,10 @@ def load() -> ctypes.CDLL:
         lib.kda_prefill_varlen.argtypes = [
             vp, vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, i32,
             i32, f32, i32, vp, sz, vp]
+        lib.kda_prefill_varlen_gated.restype = i32
+        lib.kda_prefill_varlen_gated.argtypes = [
+            vp, vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, vp, f32, vp,
+            i32, i32, i32, i32, f32, i32, vp, sz, vp]
         lib.kda_prefill_varlen_noalloc.restype = i32
         lib.kda_prefill_varlen_noalloc.argtypes = [
             vp, vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, i32, i32, i32,
@@ -315,6 +319,52 @@ def kda_prefill_varlen_recur(workspace, cu_seqlens, max_seqlen: int,
     if st != KDA_OK:
         raise KDAError("kda_prefill_varlen_recur", st)
     return o, final_state
+
+
+def kda_prefill_varlen_gated(q, k, v, g, beta, cu_seqlens, max_seqlen: int,
+                             initial_state=None, *, z, w, eps: float = 1e-6,
+                             chunk_size: int = 64, scale: float = 1.0,
+                             output_final_state: bool = True,
+                             final_state=None, y=None, workspace=None):
+    """kda_prefill_varlen with the output epilogue fused into the recurrence:
+    returns (y, final_state) with y = o * rsqrt(mean(o^2) + eps) * w *
+    sigmoid(z) per (token, head) row.  z: [total_T, H, Dv] (dtype of q);
+    w: [Dv] fp32."""
+    lib = load()
+    total_T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    N = cu_seqlens.numel() - 1
+    for t, n, s, dt in ((q, "q", (total_T, H, Dk), q.dtype),
+                        (k, "k", (total_T, H, Dk), q.dtype),
+                        (v, "v", (total_T, H, Dv), q.dtype),
+                        (g, "g", (total_T, H, Dk), torch.float32),
+                        (beta, "beta", (total_T, H), torch.float32),
+                        (cu_seqlens, "cu_seqlens", (N + 1,), torch.int32),
+                        (z, "z", (total_T, H, Dv), q.dtype),
+                        (w, "w", (Dv,), torch.float32)):
+        _check(t, n, s, dt, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (N, H, Dk, Dv), torch.float32,
+               dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32,
+                                  device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (N, H, Dk, Dv), torch.float32, dev)
+    if y is None:
+        y = torch.empty((total_T, H, Dv), dtype=q.dtype, device=dev)
+    _check(y, "y", (total_T, H, Dv), q.dtype, dev)
+    if workspace is None:
+        workspace = workspace_for(N, total_T, H, Dk, Dv, chunk_size, dev)
+    st = lib.kda_prefill_varlen_gated(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N,
+        total_T, int(max_seqlen), _ptr(initial_state), _ptr(final_state),
+        _ptr(z), _ptr(w), float(eps), _ptr(y), H, Dk, Dv, chunk_size, scale,
+        _dtype_code(q), _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_prefill_varlen_gated", st)
+    return y, final_state
 
 
 def kda_prefill_varlen_noalloc(q, k, v, g, beta, cu_seqlens,

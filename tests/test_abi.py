@@ -35,6 +35,7 @@ def test_exports_every_declared_symbol():
                           "kda_prefill_varlen", "kda_prefill_varlen_ckpt",
                           "kda_prefill_varlen_ckpt_at",
                           "kda_prefill_varlen_noalloc",
+                          "kda_prefill_varlen_gated",
                           "kda_decode_step", "kda_spec_verify",
                           "kda_spec_commit", "kda_output_norm_gate",
                           "kda_decode_step_gated",
@@ -139,6 +140,33 @@ def test_prefill_varlen_validation():
     assert _varlen(lib, C=8) == UNSUP
     assert _varlen(lib, ws_bytes=10) == WS
     assert _varlen(lib, v=NULL) == INVALID
+
+
+def _gated(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, cu=P, N=2, total=100, maxlen=64,
+             s0=NULL, s1=NULL, z=P, w=P, eps=1e-6, y=P, H=2, Dk=64, Dv=64,
+             C=64, scale=1.0, dtype=0, ws=P, ws_bytes=1 << 40, stream=NULL)
+    a.update(kw)
+    return lib.kda_prefill_varlen_gated(
+        a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"],
+        a["total"], a["maxlen"], a["s0"], a["s1"], a["z"], a["w"], a["eps"],
+        a["y"], a["H"], a["Dk"], a["Dv"], a["C"], a["scale"], a["dtype"],
+        a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_prefill_varlen_gated_validation():
+    """Every call here fails validation (nothing is launched)."""
+    lib = kda.load()
+    assert _gated(lib, z=NULL) == INVALID
+    assert _gated(lib, w=NULL) == INVALID
+    assert _gated(lib, z=MIS) == INVALID
+    assert _gated(lib, w=ctypes.c_void_p(0x100004)) == INVALID
+    assert _gated(lib, eps=-1.0) == INVALID
+    assert _gated(lib, eps=float("nan")) == INVALID
+    assert _gated(lib, y=NULL) == INVALID
+    assert _gated(lib, N=0) == INVALID
+    assert _gated(lib, C=8) == UNSUP
+    assert _gated(lib, ws_bytes=10) == WS
 
 
 def _noalloc(lib, **kw):
