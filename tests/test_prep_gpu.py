@@ -75,20 +75,25 @@ def frag_ut(js, rs, mt):
 
 def decode_block(blk, lay):
     """One workspace block (uint8 numpy) -> dict of float64 tensors."""
-    bf = lambda off, n: (  # noqa: E731  bf16 bits -> exact float
-        np.frombuffer(blk[off:off + 2 * n].tobytes(), np.uint16)
-        .astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    def bf(off, n, idx):
+        """bf16 elements idx of the n at byte offset off, as exact floats
+        (slots outside idx are never written and not converted)."""
+        bits = np.frombuffer(blk[off:off + 2 * n].tobytes(), np.uint16)[idx]
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(
+            np.float64)
     C, Dk, Dv = lay.C, lay.Dk, lay.Dv
     rc, rk, rv = np.arange(C), np.arange(Dk), np.arange(Dv)
     nW = lay.mt * lay.kst * 512
-    W = bf(lay.W, nW)[frag16(rc, rk, lay.kst)]
-    Qh = bf(lay.Qh, nW)[frag16(rc, rk, lay.kst)]
-    KbT = bf(lay.KbT, (Dk // 16) * lay.cst * 512)[frag16(rk, rc, lay.cst)]
-    UtT = bf(lay.UtT, (Dv // 16) * lay.mt * 256)[frag_ut(rv, rc, lay.mt)]
-    M = bf(lay.M, lay.mt * lay.cst * 512)[frag16(rc, rc, lay.cst)]
+    W = bf(lay.W, nW, frag16(rc, rk, lay.kst))
+    Qh = bf(lay.Qh, nW, frag16(rc, rk, lay.kst))
+    KbT = bf(lay.KbT, (Dk // 16) * lay.cst * 512, frag16(rk, rc, lay.cst))
+    UtT = bf(lay.UtT, (Dv // 16) * lay.mt * 256, frag_ut(rv, rc, lay.mt))
+    mi = frag16(rc, rc, lay.cst)
     # fragments (row tile m, column group cs) with 2 cs > m lie above the
     # diagonal: zero by definition, never written, never read
-    M[(2 * (rc[None, :] >> 5)) > (rc[:, None] >> 4)] = 0.0
+    above = (2 * (rc[None, :] >> 5)) > (rc[:, None] >> 4)
+    M = bf(lay.M, lay.mt * lay.cst * 512, np.where(above, 0, mi))
+    M[above] = 0.0
     gamma = np.frombuffer(blk[lay.gamma:lay.gamma + 4 * Dk].tobytes(),
                           np.float32)
     return dict(W=W, Qh=Qh, KbT=KbT, UtT=UtT, M=M, gamma=gamma)
