@@ -33,8 +33,15 @@
  *   (decode), sequences is B or N.
  * - q, k, v and o share one storage dtype (KDA_DTYPE_BF16 or KDA_DTYPE_FP32);
  *   g, beta and the state are always fp32.
- * - Supported sizes: Dk == Dv in {16, 32, 64, 128}; chunk size C in
- *   {16, 32, 64}.  Anything else returns KDA_ERR_UNSUPPORTED.
+ * - Supported sizes: Dk and Dv each any multiple of 16 from 16 to 128
+ *   (independently; the prologue form needs Dk == Dv); chunk size C in
+ *   {16, 32, 64}.  The kernels run on the smallest square tile of 16, 32, 64
+ *   or 128 channels that holds both dims, the channels past them being zero
+ *   inside the kernels, so e.g. Dk = 64, Dv = 128 costs what 128 x 128
+ *   costs.  Prefill also needs (C + 8) * H * tile * 4 bytes below 4 GiB
+ *   (each chunk's token rows are addressed with 32-bit buffer offsets: H up
+ *   to 116,508 at a 128 tile and C = 64).  Anything else returns
+ *   KDA_ERR_UNSUPPORTED.
  * - Preconditions that are NOT checked on the device: -5 <= g <= 0 (the
  *   bound that keeps every 16-row tile's decay factors inside the bf16
  *   range), and a valid cu_seqlens.  Violating them gives unspecified values
@@ -361,7 +368,7 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v,
  * bound by HBM bandwidth.
  *   o, z, y [tokens, H, Dv] dtype (y may be o itself); w [Dv] fp32;
  *   eps >= 0.
- * tokens >= 0 (0 enqueues nothing); H >= 1; Dv in {16, 32, 64, 128}.
+ * tokens >= 0 (0 enqueues nothing); H >= 1; Dv a multiple of 16 up to 128.
  */
 kda_status_t kda_output_norm_gate(const void* o, const void* z,
                                   const float* w, float eps, void* y,

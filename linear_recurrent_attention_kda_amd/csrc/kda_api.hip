@@ -46,8 +46,18 @@ bool aligned(const void* p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }
 
+// Head dims: any multiple of 16 up to 128, d_k and d_v independently.  The
+// kernels are compiled for square tiles of 16, 32, 64 or 128 channels; a
+// call runs on the smallest tile that holds both dims, with the channels
+// past them zero inside the kernels (the state's padded rows and columns
+// stay zero: their k, q and v entries are zero).
+bool supported_dim(int32_t d) { return d >= 16 && d <= 128 && d % 16 == 0; }
 bool supported_dims(int32_t Dk, int32_t Dv) {
-  return Dk == Dv && (Dk == 16 || Dk == 32 || Dk == 64 || Dk == 128);
+  return supported_dim(Dk) && supported_dim(Dv);
+}
+int32_t tile_dim(int32_t Dk, int32_t Dv) {
+  const int32_t m = Dk > Dv ? Dk : Dv;
+  return m <= 16 ? 16 : m <= 32 ? 32 : m <= 64 ? 64 : 128;
 }
 
 bool supported_chunk(int32_t C) { return C == 16 || C == 32 || C == 64; }
@@ -60,6 +70,12 @@ kda_status_t check_prefill_common(int32_t H, int32_t Dk, int32_t Dv,
     return KDA_ERR_UNSUPPORTED;
   if (!supported_dims(Dk, Dv) || !supported_chunk(C))
     return KDA_ERR_UNSUPPORTED;
+  // The kernels address each chunk's token rows (and the input prologue's
+  // three rows before them) through 32-bit buffer offsets, with masked
+  // lanes parked just below 2^32: C + 8 rows of H heads must stay well
+  // under 4 GiB (H <= 116,508 at d = 128, C = 64 in fp32).
+  if ((int64_t)(C + 8) * H * tile_dim(Dk, Dv) * 4 > 0xFFFF0000LL)
+    return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
 }
 
@@ -69,12 +85,13 @@ constexpr int kStagePrep = 1, kStageRecur = 2, kStagesBoth = 3;
 
 // With validate_only, every check except the workspace's runs and nothing is
 // launched.
-kda_status_t run_prefill(kda::PrefillArgs& a, int32_t D, int32_t C,
-                         int32_t dtype, void* workspace,
-                         size_t workspace_bytes, void* stream,
+kda_status_t run_prefill(kda::PrefillArgs& a, int32_t C, int32_t dtype,
+                         void* workspace, size_t workspace_bytes, void* stream,
                          int stages = kStagesBoth,
                          bool validate_only = false) {
-  const size_t need = kda_prefill_workspace_size(a.N, a.total_T, a.H, D, D, C);
+  const int32_t D = tile_dim(a.dk, a.dv);
+  const size_t need =
+      kda_prefill_workspace_size(a.N, a.total_T, a.H, a.dk, a.dv, C);
   if (need == 0) return KDA_ERR_INVALID_ARG;
   // the prep kernel indexes its (sequence, chunk, head) items in 32 bits
   if ((int64_t)a.N * a.max_chunks * a.H >= ((int64_t)1 << 31))
@@ -187,8 +204,10 @@ kda_status_t prefill_varlen(const void* q, const void* k, const void* v,
   if ((initial_state && !aligned(initial_state, 16)) ||
       (final_state && !aligned(final_state, 16)))
     return KDA_ERR_INVALID_ARG;
-  if ((int64_t)(Dv / 16) * H * N > INT_MAX)
+  if ((int64_t)(tile_dim(Dk, Dv) / 16) * H * N > INT_MAX)
     return KDA_ERR_UNSUPPORTED;
+  // the input prologue's taps are per channel of q, k and v alike
+  if (conv_w && Dk != Dv) return KDA_ERR_UNSUPPORTED;
   const int64_t maxlen = max_seqlen < total_T ? max_seqlen : total_T;
 
   kda::PrefillArgs a{};
@@ -204,13 +223,15 @@ kda_status_t prefill_varlen(const void* q, const void* k, const void* v,
   a.final_state = final_state;
   a.o = o;
   a.H = H;
+  a.dk = Dk;
+  a.dv = Dv;
   a.scale = scale;
   a.conv_w = conv_w;
   a.gate_z = gate_z;
   a.gate_w = gate_w;
   a.gate_eps = gate_eps;
-  return run_prefill(a, Dk, C, dtype, workspace, workspace_bytes, stream,
-                     stages, validate_only);
+  return run_prefill(a, C, dtype, workspace, workspace_bytes, stream, stages,
+                     validate_only);
 }
 
 kda_status_t decode_step(const void* q, const void* k, const void* v,
@@ -233,11 +254,13 @@ kda_status_t decode_step(const void* q, const void* k, const void* v,
   a.o = o;
   a.B = B;
   a.H = H;
+  a.dk = Dk;
+  a.dv = Dv;
   a.scale = scale;
   a.z = z;
   a.w = w;
   a.eps = eps;
-  if (kda::launch_decode(a, Dk, dtype == KDA_DTYPE_BF16,
+  if (kda::launch_decode(a, tile_dim(Dk, Dv), dtype == KDA_DTYPE_BF16,
                          static_cast<hipStream_t>(stream)) != hipSuccess)
     return KDA_ERR_LAUNCH;
   return KDA_OK;
@@ -267,7 +290,8 @@ size_t kda_prefill_workspace_size(int32_t N, int64_t total_T, int32_t H,
   if (N <= 0 || total_T < 0 || H <= 0 || !supported_dims(Dk, Dv) ||
       !supported_chunk(C))
     return 0;
-  const kda::WsLayout lay = kda::WsLayout::make(C, Dk, Dv);
+  const int32_t D = tile_dim(Dk, Dv);
+  const kda::WsLayout lay = kda::WsLayout::make(C, D, D);
   const int64_t slots = kda::num_slots(N, total_T, C);
   return (size_t)slots * (size_t)H * lay.block_bytes;
 }
@@ -289,7 +313,7 @@ kda_status_t kda_prefill_chunked(const void* q, const void* k, const void* v,
   if ((initial_state && !aligned(initial_state, 16)) ||
       (final_state && !aligned(final_state, 16)))
     return KDA_ERR_INVALID_ARG;
-  if ((int64_t)(Dv / 16) * H * B > INT_MAX)
+  if ((int64_t)(tile_dim(Dk, Dv) / 16) * H * B > INT_MAX)
     return KDA_ERR_UNSUPPORTED;
 
   kda::PrefillArgs a{};
@@ -303,8 +327,10 @@ kda_status_t kda_prefill_chunked(const void* q, const void* k, const void* v,
   a.final_state = final_state;
   a.o = o;
   a.H = H;
+  a.dk = Dk;
+  a.dv = Dv;
   a.scale = scale;
-  return run_prefill(a, Dk, C, dtype, workspace, workspace_bytes, stream);
+  return run_prefill(a, C, dtype, workspace, workspace_bytes, stream);
 }
 
 kda_status_t kda_prefill_varlen(const void* q, const void* k, const void* v,
@@ -342,7 +368,8 @@ kda_status_t kda_prefill_varlen_gated(
   if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
   const int64_t rows = total_T * H;  // the epilogue's grid, as in its entry
-  if (rows / (1024 / Dv) >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
+  if (rows / (1024 / tile_dim(Dv, Dv)) >= ((int64_t)1 << 31))
+    return KDA_ERR_UNSUPPORTED;
   // The fused kernel holds whole rows, i.e. one workgroup per (sequence,
   // head) instead of one per d_v slice.  Measured on MI355X it is faster
   // than the plain recurrence followed by the epilogue pass once there are
@@ -362,8 +389,9 @@ kda_status_t kda_prefill_varlen_gated(
   kda::EpilogueArgs e{};
   e.o = y; e.z = z; e.w = w; e.y = y;
   e.rows = rows;
+  e.dv = Dv;
   e.eps = eps;
-  if (kda::launch_epilogue(e, Dv, dtype == KDA_DTYPE_BF16,
+  if (kda::launch_epilogue(e, tile_dim(Dv, Dv), dtype == KDA_DTYPE_BF16,
                            static_cast<hipStream_t>(stream)) != hipSuccess)
     return KDA_ERR_LAUNCH;
   return KDA_OK;
@@ -506,20 +534,22 @@ kda_status_t kda_output_norm_gate(const void* o, const void* z,
     return KDA_ERR_INVALID_ARG;
   if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_FP32)
     return KDA_ERR_UNSUPPORTED;
-  if (!supported_dims(Dv, Dv)) return KDA_ERR_UNSUPPORTED;
+  if (!supported_dim(Dv)) return KDA_ERR_UNSUPPORTED;
   if (tokens == 0) return KDA_OK;
   if (!o || !z || !w || !y) return KDA_ERR_INVALID_ARG;
   if (!aligned(o, 16) || !aligned(z, 16) || !aligned(w, 16) ||
       !aligned(y, 16))
     return KDA_ERR_INVALID_ARG;
   const int64_t rows = tokens * H;
-  // the grid covers rows in groups of 256 / (Dv / 4)
-  if (rows / (1024 / Dv) >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
+  // the grid covers rows in groups of 256 / (D / 4), D the tile
+  const int32_t D = tile_dim(Dv, Dv);
+  if (rows / (1024 / D) >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
   kda::EpilogueArgs a{};
   a.o = o; a.z = z; a.w = w; a.y = y;
   a.rows = rows;
+  a.dv = Dv;
   a.eps = eps;
-  if (kda::launch_epilogue(a, Dv, dtype == KDA_DTYPE_BF16,
+  if (kda::launch_epilogue(a, D, dtype == KDA_DTYPE_BF16,
                            static_cast<hipStream_t>(stream)) != hipSuccess)
     return KDA_ERR_LAUNCH;
   return KDA_OK;
@@ -547,8 +577,9 @@ kda_status_t kda_spec_verify(const void* q, const void* k, const void* v,
   a.o = o;
   a.u = u;
   a.B = B; a.T = T; a.H = H;
+  a.dk = Dk; a.dv = Dv;
   a.scale = scale;
-  if (kda::launch_spec(a, Dk, dtype == KDA_DTYPE_BF16, false,
+  if (kda::launch_spec(a, tile_dim(Dk, Dv), dtype == KDA_DTYPE_BF16, false,
                        static_cast<hipStream_t>(stream)) != hipSuccess)
     return KDA_ERR_LAUNCH;
   return KDA_OK;
@@ -575,7 +606,8 @@ kda_status_t kda_spec_commit(const void* k, const float* g, const float* u,
   a.accepted = accepted;
   a.state = state;
   a.B = B; a.T = T; a.H = H;
-  if (kda::launch_spec(a, Dk, dtype == KDA_DTYPE_BF16, true,
+  a.dk = Dk; a.dv = Dv;
+  if (kda::launch_spec(a, tile_dim(Dk, Dv), dtype == KDA_DTYPE_BF16, true,
                        static_cast<hipStream_t>(stream)) != hipSuccess)
     return KDA_ERR_LAUNCH;
   return KDA_OK;

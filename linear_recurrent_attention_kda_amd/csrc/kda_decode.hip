@@ -50,23 +50,32 @@ void decode_kernel(DecodeArgs a) {
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
   const int cg = tid % CG, rg = tid / CG;
-  float* S = a.state + (size_t)bh * D * D;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, D * D * 4);
+  // the stored slice is dk x dv (<= D x D); rows past dk and column groups
+  // past dv are zero here and never stored
+  const int dk = a.dk, dv = a.dv;
+  const bool col_ok = 4 * cg < dv;
+  float* S = a.state + (size_t)bh * dk * dv;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, dk * dv * 4);
   constexpr int kPol = kNt ? kCachePolicyNt : 0;
+  auto soff = [&](int c) {
+    return (c < dk && col_ok) ? (uint32_t)((c * dv + 4 * cg) * 4) : kOffNone;
+  };
 
   float4 s[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
     s[i] = __builtin_bit_cast(
-        float4, __builtin_amdgcn_raw_buffer_load_b128(
-                    rs, ((rg + RG * i) * D + 4 * cg) * 4, 0, kPol));
+        float4, __builtin_amdgcn_raw_buffer_load_b128(rs, soff(rg + RG * i),
+                                                      0, kPol));
 
-  const Tio* q = static_cast<const Tio*>(a.q) + (size_t)bh * D;
-  const Tio* k = static_cast<const Tio*>(a.k) + (size_t)bh * D;
+  const Tio* q = static_cast<const Tio*>(a.q) + (size_t)bh * dk;
+  const Tio* k = static_cast<const Tio*>(a.k) + (size_t)bh * dk;
   if (tid < D) {
-    s_alpha[tid] = __builtin_amdgcn_exp2f(a.g[(size_t)bh * D + tid] * kLog2e);
-    s_k[tid] = io<Tio>::to_f(k[tid]);
-    s_q[tid] = io<Tio>::to_f(q[tid]);
+    const bool ok = tid < dk;
+    s_alpha[tid] =
+        ok ? __builtin_amdgcn_exp2f(a.g[(size_t)bh * dk + tid] * kLog2e) : 1.f;
+    s_k[tid] = ok ? io<Tio>::to_f(k[tid]) : 0.f;
+    s_q[tid] = ok ? io<Tio>::to_f(q[tid]) : 0.f;
   }
   __syncthreads();
 
@@ -135,13 +144,18 @@ void decode_kernel(DecodeArgs a) {
     }
   }
 
-  const Tio* v = static_cast<const Tio*>(a.v) + (size_t)bh * D + 4 * cg;
+  const Tio* v = static_cast<const Tio*>(a.v) + (size_t)bh * dv + 4 * cg;
   const float beta = a.beta[bh];
+  float vv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (col_ok) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vv[i] = io<Tio>::to_f(v[i]);
+  }
   float4 u;
-  u.x = beta * (io<Tio>::to_f(v[0]) - X.x);
-  u.y = beta * (io<Tio>::to_f(v[1]) - X.y);
-  u.z = beta * (io<Tio>::to_f(v[2]) - X.z);
-  u.w = beta * (io<Tio>::to_f(v[3]) - X.w);
+  u.x = beta * (vv[0] - X.x);
+  u.y = beta * (vv[1] - X.y);
+  u.z = beta * (vv[2] - X.z);
+  u.w = beta * (vv[3] - X.w);
 
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
@@ -151,12 +165,12 @@ void decode_kernel(DecodeArgs a) {
     w.x = s[i].x + kc * u.x; w.y = s[i].y + kc * u.y;
     w.z = s[i].z + kc * u.z; w.w = s[i].w + kc * u.w;
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), rs,
-                                           (c * D + 4 * cg) * 4, 0, kPol);
+                                           soff(c), 0, kPol);
   }
 
   // output (after the state stores, so that the state's registers are free)
   if (rg == 0) {
-    Tio* o = static_cast<Tio*>(a.o) + (size_t)bh * D + 4 * cg;
+    Tio* o = static_cast<Tio*>(a.o) + (size_t)bh * dv + 4 * cg;
     float ov[4] = {a.scale * (Y.x + QK * u.x), a.scale * (Y.y + QK * u.y),
                    a.scale * (Y.z + QK * u.z), a.scale * (Y.w + QK * u.w)};
     if (kGated) {
@@ -166,17 +180,21 @@ void decode_kernel(DecodeArgs a) {
       float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
 #pragma unroll
       for (int m = CG / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-      const float r = rsqrtf(ss * (1.f / D) + a.eps);
-      const Tio* z = static_cast<const Tio*>(a.z) + (size_t)bh * D + 4 * cg;
+      const float r = rsqrtf(ss / (float)dv + a.eps);
+      const Tio* z = static_cast<const Tio*>(a.z) + (size_t)bh * dv + 4 * cg;
+      if (col_ok) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float gate = 1.f / (1.f + __builtin_amdgcn_exp2f(
-                                            -io<Tio>::to_f(z[i]) * kLog2e));
-        ov[i] = ov[i] * r * a.w[4 * cg + i] * gate;
+        for (int i = 0; i < 4; ++i) {
+          const float gate = 1.f / (1.f + __builtin_amdgcn_exp2f(
+                                              -io<Tio>::to_f(z[i]) * kLog2e));
+          ov[i] = ov[i] * r * a.w[4 * cg + i] * gate;
+        }
       }
     }
+    if (col_ok) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = io<Tio>::from_f(ov[i]);
+      for (int i = 0; i < 4; ++i) o[i] = io<Tio>::from_f(ov[i]);
+    }
   }
 
 }

@@ -159,6 +159,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes,
                                            0x00020000);
 }
+// A buffer offset past every buffer the kernels build (each covers less than
+// 4 GiB - 256 bytes): a masked lane's load through it returns 0 and its store
+// is dropped, without a branch around the memory instruction.
+constexpr uint32_t kOffNone = 0xFFFFFF00u;
+
 // Cache-policy operand of the buffer intrinsics on gfx950: the "nt"
 // (non-temporal, streaming) bit.
 constexpr int kCachePolicyNt = 2;

@@ -65,21 +65,27 @@ __global__ __launch_bounds__(kEpiThreads) void norm_gate_kernel(EpilogueArgs a) 
   // rows past the end fall outside the buffers (loads 0, stores dropped)
   const int64_t first = (int64_t)blockIdx.x * RPB;
   const int64_t nrows = a.rows - first < RPB ? a.rows - first : RPB;
-  const uint32_t bytes = (uint32_t)(nrows * D * sizeof(Tio));
+  // rows hold dv <= D channels; lanes past them read 0 and store nothing
+  const int dv = a.dv;
+  const bool col_ok = 4 * lr < dv;
+  const uint32_t bytes = (uint32_t)(nrows * dv * sizeof(Tio));
   const __amdgpu_buffer_rsrc_t ro =
-      make_rsrc(static_cast<const Tio*>(a.o) + first * D, bytes);
+      make_rsrc(static_cast<const Tio*>(a.o) + first * dv, bytes);
   const __amdgpu_buffer_rsrc_t rz =
-      make_rsrc(static_cast<const Tio*>(a.z) + first * D, bytes);
+      make_rsrc(static_cast<const Tio*>(a.z) + first * dv, bytes);
   const __amdgpu_buffer_rsrc_t ry =
-      make_rsrc(static_cast<Tio*>(a.y) + first * D, bytes);
-  const uint32_t off = (uint32_t)(((row - first) * D + 4 * lr) * sizeof(Tio));
+      make_rsrc(static_cast<Tio*>(a.y) + first * dv, bytes);
+  const uint32_t off =
+      col_ok ? (uint32_t)(((row - first) * dv + 4 * lr) * sizeof(Tio))
+             : kOffNone;
   const f32x4 o = Vec4<Tio>::load(ro, off);
   const f32x4 z = Vec4<Tio>::load(rz, off);
-  const float4 w = *reinterpret_cast<const float4*>(a.w + 4 * lr);
+  const float4 w = col_ok ? *reinterpret_cast<const float4*>(a.w + 4 * lr)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
   float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-  const float r = rsqrtf(ss * (1.f / D) + a.eps);
+  const float r = rsqrtf(ss / (float)dv + a.eps);
   const float wv[4] = {w.x, w.y, w.z, w.w};
   f32x4 y;
 #pragma unroll

@@ -79,6 +79,10 @@ struct PrefillArgs {
   float* final_state;
   void* o;
   int32_t H;
+  // head dims as stored (multiples of 16, at most the kernels' tile D):
+  // rows of q, k, g and of the state hold dk channels, rows of v, o and the
+  // state's columns dv; channels past them are zero inside the kernels
+  int32_t dk, dv;
   float scale;
   char* ws;
   int64_t nslots;
@@ -113,6 +117,7 @@ struct SpecArgs {
   float* u;                                      // [B, T, H, D] fp32
   const int32_t* accepted;                       // [B] (commit)
   int32_t B, T, H;
+  int32_t dk, dv;                                // head dims as stored
   float scale;
 };
 
@@ -121,6 +126,7 @@ struct DecodeArgs {
   const float* g; const float* beta;
   float* state; void* o;
   int32_t B, H;
+  int32_t dk, dv;                                // head dims as stored
   float scale;
   // output epilogue fused into the decode step (when z != nullptr): o is
   // replaced by o * rsqrt(mean(o^2) + eps) * w * sigmoid(z)
@@ -130,6 +136,7 @@ struct DecodeArgs {
 struct EpilogueArgs {
   const void* o; const void* z; const float* w; void* y;
   int64_t rows;                // tokens * heads
+  int32_t dv;                  // channels of a row as stored
   float eps;
 };
 

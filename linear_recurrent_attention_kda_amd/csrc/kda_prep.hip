@@ -184,19 +184,32 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a) {
   //         outside the buffers and load as 0 --------------------------------
   const int64_t row0 = it.t0 * H + h;
   const int64_t span = (int64_t)(it.L - 1) * H;
+  // rows hold dk (q, k, g) and dv (v) channels as stored, at most the tile
+  // D; the channel groups past them load 0 (their offset is out of range),
+  // so the padded channels of every tensor formed below are exact zeros
+  const int dk = a.dk, dv = a.dv;
+  const bool kc_ok = c0 < dk, vc_ok = c0 < dv;
   const __amdgpu_buffer_rsrc_t Rq = make_rsrc(
-      static_cast<const Tin*>(a.q) + row0 * K,
-      (uint32_t)((span * K + K) * sizeof(Tin)));
+      static_cast<const Tin*>(a.q) + row0 * dk,
+      (uint32_t)((span * dk + dk) * sizeof(Tin)));
   const __amdgpu_buffer_rsrc_t Rk = make_rsrc(
-      static_cast<const Tin*>(a.k) + row0 * K,
-      (uint32_t)((span * K + K) * sizeof(Tin)));
+      static_cast<const Tin*>(a.k) + row0 * dk,
+      (uint32_t)((span * dk + dk) * sizeof(Tin)));
   const __amdgpu_buffer_rsrc_t Rv = make_rsrc(
-      static_cast<const Tin*>(a.v) + row0 * V,
-      (uint32_t)((span * V + V) * sizeof(Tin)));
+      static_cast<const Tin*>(a.v) + row0 * dv,
+      (uint32_t)((span * dv + dv) * sizeof(Tin)));
   const __amdgpu_buffer_rsrc_t Rg =
-      make_rsrc(a.g + row0 * K, (uint32_t)((span * K + K) * 4));
+      make_rsrc(a.g + row0 * dk, (uint32_t)((span * dk + dk) * 4));
   const __amdgpu_buffer_rsrc_t Rb =
       make_rsrc(a.beta + row0, (uint32_t)((span + 1) * 4));
+  // byte offsets of channel group c0 (plus e elements) in row `row` (a
+  // multiple of H) of an input with `es`-byte elements, or out of range
+  auto koff = [&](uint32_t row, uint32_t es, uint32_t e = 0) {
+    return kc_ok ? (row * (uint32_t)dk + c0 + e) * es : kOffNone + e * es;
+  };
+  auto voff = [&](uint32_t row, uint32_t es) {
+    return vc_ok ? (row * (uint32_t)dv + c0) * es : kOffNone;
+  };
 
   float gx[RPT][8], bt[RPT];
   Raw8<Tin> rq[RPT], rk[RPT], rv[RPT];
@@ -207,8 +220,8 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a) {
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const uint32_t row = (uint32_t)((r0 + i) * H);
-        const uint4 g0 = buffer_load_16(Rg, (row * K + c0) * 4);
-        const uint4 g1 = buffer_load_16(Rg, (row * K + c0 + 4) * 4);
+        const uint4 g0 = buffer_load_16(Rg, koff(row, 4));
+        const uint4 g1 = buffer_load_16(Rg, koff(row, 4, 4));
         gx[i][0] = __uint_as_float(g0.x); gx[i][1] = __uint_as_float(g0.y);
         gx[i][2] = __uint_as_float(g0.z); gx[i][3] = __uint_as_float(g0.w);
         gx[i][4] = __uint_as_float(g1.x); gx[i][5] = __uint_as_float(g1.y);
@@ -220,9 +233,9 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a) {
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const uint32_t row = (uint32_t)((r0 + i) * H);
-        rq[i].load_buf(Rq, (row * K + c0) * sizeof(Tin));
-        rk[i].load_buf(Rk, (row * K + c0) * sizeof(Tin));
-        rv[i].load_buf(Rv, (row * V + c0) * sizeof(Tin));
+        rq[i].load_buf(Rq, koff(row, sizeof(Tin)));
+        rk[i].load_buf(Rk, koff(row, sizeof(Tin)));
+        rv[i].load_buf(Rv, voff(row, sizeof(Tin)));
       }
     } else {
 #pragma unroll
@@ -250,37 +263,38 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a) {
     const int64_t wrow0 = wb * H + h;
     const int64_t wspan = (it.t0 + it.L - 1 - wb) * H;
     const __amdgpu_buffer_rsrc_t Wq = make_rsrc(
-        static_cast<const Tin*>(a.q) + wrow0 * K,
-        (uint32_t)((wspan * K + K) * sizeof(Tin)));
+        static_cast<const Tin*>(a.q) + wrow0 * dk,
+        (uint32_t)((wspan * dk + dk) * sizeof(Tin)));
     const __amdgpu_buffer_rsrc_t Wk = make_rsrc(
-        static_cast<const Tin*>(a.k) + wrow0 * K,
-        (uint32_t)((wspan * K + K) * sizeof(Tin)));
+        static_cast<const Tin*>(a.k) + wrow0 * dk,
+        (uint32_t)((wspan * dk + dk) * sizeof(Tin)));
     const __amdgpu_buffer_rsrc_t Wv = make_rsrc(
-        static_cast<const Tin*>(a.v) + wrow0 * V,
-        (uint32_t)((wspan * V + V) * sizeof(Tin)));
+        static_cast<const Tin*>(a.v) + wrow0 * dv,
+        (uint32_t)((wspan * dv + dv) * sizeof(Tin)));
     // Issue order: the head's taps (small, shared by all of the head's
     // chunks), then a and b, then the convolution windows.  Loads complete
     // in order, so storing the taps to LDS waits for the taps only, and the
     // gates wait for a and b only, while the windows are still arriving.
-    // taps of this head: [3][D][4] fp32, staged in LDS
+    // taps of this head: [3][dk][4] fp32 as stored (dk == dv here), staged
+    // in LDS as [3][D][4] with the padded channels' taps 0
     constexpr int NTAP = 3 * D * kConvTaps;
     constexpr int TPT = (NTAP + NT - 1) / NT;  // taps per thread
-    const float* taps = a.conv_w + (size_t)h * D * kConvTaps;
+    const float* taps = a.conv_w + (size_t)h * dk * kConvTaps;
     float tapv[TPT];
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
       const int e = tid + u * NT;
       const int x = e / (D * kConvTaps), rem = e % (D * kConvTaps);
-      tapv[u] = (NTAP % NT == 0 || e < NTAP)
-                    ? taps[(size_t)x * H * D * kConvTaps + rem] : 0.f;
+      tapv[u] = ((NTAP % NT == 0 || e < NTAP) && rem < dk * kConvTaps)
+                    ? taps[(size_t)x * H * dk * kConvTaps + rem] : 0.f;
     }
     float av[RPT][8];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const uint32_t row = (uint32_t)((r0 + i) * H);
       if (active) {
-        const uint4 g0 = buffer_load_16(Rg, (row * K + c0) * 4);
-        const uint4 g1 = buffer_load_16(Rg, (row * K + c0 + 4) * 4);
+        const uint4 g0 = buffer_load_16(Rg, koff(row, 4));
+        const uint4 g1 = buffer_load_16(Rg, koff(row, 4, 4));
         av[i][0] = __uint_as_float(g0.x); av[i][1] = __uint_as_float(g0.y);
         av[i][2] = __uint_as_float(g0.z); av[i][3] = __uint_as_float(g0.w);
         av[i][4] = __uint_as_float(g1.x); av[i][5] = __uint_as_float(g1.y);
@@ -300,9 +314,9 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a) {
     for (int j = 0; j < NWIN; ++j) {
       const uint32_t row = (uint32_t)((d0 + j) * H);
       if (active) {
-        wq[j].load_buf(Wq, (row * K + c0) * sizeof(Tin));
-        wk[j].load_buf(Wk, (row * K + c0) * sizeof(Tin));
-        wv[j].load_buf(Wv, (row * V + c0) * sizeof(Tin));
+        wq[j].load_buf(Wq, koff(row, sizeof(Tin)));
+        wk[j].load_buf(Wk, koff(row, sizeof(Tin)));
+        wv[j].load_buf(Wv, voff(row, sizeof(Tin)));
       } else {
         wq[j].zero();
         wk[j].zero();
@@ -322,13 +336,14 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a) {
     // selected, so that no branch surrounds it
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      // rows past L must keep g = 0 and beta = 0 (no decay, no write)
+      // rows past L must keep g = 0 and beta = 0 (no decay, no write), and
+      // so must the padded channels (g = 0)
       const bool live = r0 + i < it.L;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float sg = __builtin_amdgcn_rcpf(
             1.f + __builtin_amdgcn_exp2f(-av[i][e] * kLog2e));
-        gx[i][e] = live ? -5.f * sg : 0.f;
+        gx[i][e] = (live && kc_ok) ? -5.f * sg : 0.f;
       }
       const float sb = __builtin_amdgcn_rcpf(
           1.f + __builtin_amdgcn_exp2f(-bt[i] * kLog2e));

@@ -87,6 +87,11 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
   const int n = bid / (NVT * a.H);
   const int j0 = vt * BV;
   const int H = a.H;
+  // the stored state and output rows hold dk x dv and dv channels (<= D):
+  // a slice entirely past dv has nothing to do; padded rows and columns are
+  // zero in the accumulators and never stored
+  const int dk = a.dk, dv = a.dv;
+  if (j0 >= dv) return;  // uniform over the workgroup
 
   int64_t bos, eos;
   seq_bounds(a, n, bos, eos);
@@ -115,7 +120,11 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
   // ---- initial state -> accumulators (D layout: row c = 16ct + 4kg + e,
   //      column j = 16jt + rl) and its bf16 copy -----------------------------
   f32x4 S[SPW];
-  const size_t sbase = ((size_t)n * H + h) * (size_t)K * V;
+  const size_t sbase = ((size_t)n * H + h) * (size_t)dk * dv;
+  // element (row, col) of a stored dk x dv state slice, -1 when padded
+  auto sidx = [&](int row, int col) -> int64_t {
+    return (row < dk && col < dv) ? (int64_t)row * dv + col : -1;
+  };
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
     const int t = s0t + i;
@@ -124,9 +133,10 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
       const int ct = t / JT, jt = t % JT;
       if (a.initial_state) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          S[i][e] = a.initial_state[sbase + (size_t)(16 * ct + 4 * kg + e) * V +
-                                    j0 + 16 * jt + rl];
+        for (int e = 0; e < 4; ++e) {
+          const int64_t ix = sidx(16 * ct + 4 * kg + e, j0 + 16 * jt + rl);
+          S[i][e] = ix >= 0 ? a.initial_state[sbase + ix] : 0.f;
+        }
       }
       bf16x4 sb;
 #pragma unroll
@@ -219,6 +229,14 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
   };
 
   Tout* o = static_cast<Tout*>(a.o);
+  // byte offset of this lane's 4 outputs in row r, tile jt of the chunk's
+  // output buffer (base at column j0), or out of range past dv
+  auto ooff = [&](int r, int jt) -> uint32_t {
+    return j0 + 16 * jt + 4 * kg < dv
+               ? (uint32_t)(((int64_t)r * H * dv + 16 * jt + 4 * kg) *
+                            sizeof(Tout))
+               : kOffNone;
+  };
 
   // One chunk of the recurrence with its operands already in registers;
   // each operand group is refilled with chunk `next` once consumed.
@@ -228,8 +246,8 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
     const int L = (eos - t0) < C ? (int)(eos - t0) : C;
     // outputs of this chunk and slice: rows r < L at stride H*V elements
     const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(
-        o + (t0 * H + h) * (int64_t)V + j0,
-        (uint32_t)(((int64_t)(L - 1) * H * V + BV) * sizeof(Tout)));
+        o + (t0 * H + h) * (int64_t)dv + j0,
+        (uint32_t)(((int64_t)(L - 1) * H * dv + BV) * sizeof(Tout)));
     __syncthreads();  // S^T copy complete; U^T buffer free
 
     // U = U~ - W S,  O^T = S^T Q^^T.  Every S^T fragment of the phase is
@@ -288,17 +306,18 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
     f32x4 zg[kGated ? UPW : 1], wg[kGated ? UPW : 1];
     if constexpr (kGated) {
       const __amdgpu_buffer_rsrc_t zrsrc = make_rsrc(
-          static_cast<const Tout*>(a.gate_z) + (t0 * H + h) * (int64_t)V,
-          (uint32_t)(((int64_t)(L - 1) * H * V + V) * sizeof(Tout)));
+          static_cast<const Tout*>(a.gate_z) + (t0 * H + h) * (int64_t)dv,
+          (uint32_t)(((int64_t)(L - 1) * H * dv + dv) * sizeof(Tout)));
 #pragma unroll
       for (int i = 0; i < UPW; ++i) {
         const int jt = (u0 + i) % JT;
         const int r = 16 * mrow + rl;
         zg[i] = load4(static_cast<const Tout*>(nullptr), zrsrc,
-                      (uint32_t)(((int64_t)r * H * V + 16 * jt + 4 * kg) *
-                                 sizeof(Tout)));
-        const float4 w4 = *reinterpret_cast<const float4*>(
-            a.gate_w + 16 * jt + 4 * kg);
+                      ooff(r, jt));
+        const float4 w4 =
+            16 * jt + 4 * kg < dv
+                ? *reinterpret_cast<const float4*>(a.gate_w + 16 * jt + 4 * kg)
+                : make_float4(0.f, 0.f, 0.f, 0.f);
         wg[i] = f32x4{w4.x, w4.y, w4.z, w4.w};
       }
     }
@@ -315,8 +334,7 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
         if constexpr (!kGated) {
           const int r = 16 * mrow + rl;
           buffer_store4(o, orsrc,
-                        (uint32_t)(((int64_t)r * H * V + 16 * jt + 4 * kg) *
-                                   sizeof(Tout)),
+                        ooff(r, jt),
                         Ot[i], a.scale);
         }
       }
@@ -349,7 +367,7 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
         for (int w2 = 0; w2 < NW; ++w2)
           if (w2 * UPW < NUT && (w2 * UPW) / JT == mrow) ss += s_ss[w2][rl];
       }
-      const float rn = rsqrtf(ss * (1.f / V) + a.gate_eps);
+      const float rn = rsqrtf(ss / (float)dv + a.gate_eps);
 #pragma unroll
       for (int i = 0; i < UPW; ++i) {
         if (kAllU || u0 + i < NUT) {
@@ -363,8 +381,7 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
             y[e] = Ot[i][e] * a.scale * rn * wg[i][e] * gate;
           }
           buffer_store4(o, orsrc,
-                        (uint32_t)(((int64_t)r * H * V + 16 * jt + 4 * kg) *
-                                   sizeof(Tout)),
+                        ooff(r, jt),
                         y, 1.f);
         }
       }
@@ -399,16 +416,17 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
     if (kCkpt) {
       const int64_t done = (ci + 1) * C < eos - bos ? (ci + 1) * C : eos - bos;
       while (ck.due(done)) {
-        float* dst = a.ckpt_states + ((size_t)ck.slot * H + h) * (size_t)K * V;
+        float* dst = a.ckpt_states + ((size_t)ck.slot * H + h) * (size_t)dk * dv;
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
           const int t = s0t + i;
           if (kAllS || t < NST) {
             const int ct = t / JT, jt = t % JT;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              dst[(size_t)(16 * ct + 4 * kg + e) * V + j0 + 16 * jt + rl] =
-                  S[i][e];
+            for (int e = 0; e < 4; ++e) {
+              const int64_t ix = sidx(16 * ct + 4 * kg + e, j0 + 16 * jt + rl);
+              if (ix >= 0) dst[ix] = S[i][e];
+            }
           }
         }
         ck.next();
@@ -460,9 +478,10 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
       if (t < NST) {
         const int ct = t / JT, jt = t % JT;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          a.final_state[sbase + (size_t)(16 * ct + 4 * kg + e) * V + j0 +
-                        16 * jt + rl] = S[i][e];
+        for (int e = 0; e < 4; ++e) {
+          const int64_t ix = sidx(16 * ct + 4 * kg + e, j0 + 16 * jt + rl);
+          if (ix >= 0) a.final_state[sbase + ix] = S[i][e];
+        }
       }
     }
   }
@@ -534,6 +553,9 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
   const int n = bid / (NVT * a.H);
   const int j0 = vt * BV;
   const int H = a.H;
+  // stored dims (<= D); see recur_kernel
+  const int dk = a.dk, dv = a.dv;
+  if (j0 >= dv) return;  // uniform: every wave, the loader included
 
   int64_t bos, eos;
   seq_bounds(a, n, bos, eos);
@@ -608,7 +630,11 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
   const int ct0 = s0t / JT;
 
   f32x4 S[SPW];
-  const size_t sbase = ((size_t)n * H + h) * (size_t)K * V;
+  const size_t sbase = ((size_t)n * H + h) * (size_t)dk * dv;
+  // element (row, col) of a stored dk x dv state slice, -1 when padded
+  auto sidx = [&](int row, int col) -> int64_t {
+    return (row < dk && col < dv) ? (int64_t)row * dv + col : -1;
+  };
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
     const int t = s0t + i;
@@ -616,9 +642,10 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
     S[i] = zero4();
     if (a.initial_state) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        S[i][e] = a.initial_state[sbase + (size_t)(16 * ct + 4 * kg + e) * V +
-                                  j0 + 16 * jt + rl];
+      for (int e = 0; e < 4; ++e) {
+        const int64_t ix = sidx(16 * ct + 4 * kg + e, j0 + 16 * jt + rl);
+        S[i][e] = ix >= 0 ? a.initial_state[sbase + ix] : 0.f;
+      }
     }
     bf16x4 sb;
 #pragma unroll
@@ -627,13 +654,19 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
   }
 
   Tout* o = static_cast<Tout*>(a.o);
+  auto ooff = [&](int r, int jt) -> uint32_t {  // as in recur_kernel
+    return j0 + 16 * jt + 4 * kg < dv
+               ? (uint32_t)(((int64_t)r * H * dv + 16 * jt + 4 * kg) *
+                            sizeof(Tout))
+               : kOffNone;
+  };
   for (int64_t ci = 0; ci < nchunks; ++ci) {
     const char* ob = &s_ops[ci & 1][0];
     const int64_t t0 = bos + ci * C;
     const int L = (eos - t0) < C ? (int)(eos - t0) : C;
     const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(
-        o + (t0 * H + h) * (int64_t)V + j0,
-        (uint32_t)(((int64_t)(L - 1) * H * V + BV) * sizeof(Tout)));
+        o + (t0 * H + h) * (int64_t)dv + j0,
+        (uint32_t)(((int64_t)(L - 1) * H * dv + BV) * sizeof(Tout)));
     __syncthreads();  // X_ci: S^T copy complete, U^T free, operands landed
 
     // U = U~ - W S,  O^T = S^T Q^^T
@@ -708,8 +741,7 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
         if (2 * cs <= mrow) Ot[i] = mfma_bf16(ubf[jt][cs], mf[cs], Ot[i]);
       const int r = 16 * mrow + rl;
       buffer_store4(o, orsrc,
-                    (uint32_t)(((int64_t)r * H * V + 16 * jt + 4 * kg) *
-                               sizeof(Tout)),
+                    ooff(r, jt),
                     Ot[i], a.scale);
     }
 
@@ -735,15 +767,16 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
     if (kCkpt) {
       const int64_t done = (ci + 1) * C < eos - bos ? (ci + 1) * C : eos - bos;
       while (ck.due(done)) {
-        float* dst = a.ckpt_states + ((size_t)ck.slot * H + h) * (size_t)K * V;
+        float* dst = a.ckpt_states + ((size_t)ck.slot * H + h) * (size_t)dk * dv;
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
           const int t = s0t + i;
           const int ct = t / JT, jt = t % JT;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            dst[(size_t)(16 * ct + 4 * kg + e) * V + j0 + 16 * jt + rl] =
-                S[i][e];
+          for (int e = 0; e < 4; ++e) {
+            const int64_t ix = sidx(16 * ct + 4 * kg + e, j0 + 16 * jt + rl);
+            if (ix >= 0) dst[ix] = S[i][e];
+          }
         }
         ck.next();
       }
@@ -756,9 +789,10 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
       const int t = s0t + i;
       const int ct = t / JT, jt = t % JT;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        a.final_state[sbase + (size_t)(16 * ct + 4 * kg + e) * V + j0 +
-                      16 * jt + rl] = S[i][e];
+      for (int e = 0; e < 4; ++e) {
+        const int64_t ix = sidx(16 * ct + 4 * kg + e, j0 + 16 * jt + rl);
+        if (ix >= 0) a.final_state[sbase + ix] = S[i][e];
+      }
     }
   }
 }

@@ -57,21 +57,34 @@ __global__ __launch_bounds__(NT) void spec_verify_kernel(SpecArgs a) {
   const int tid = threadIdx.x;
   const int cg = tid % CG, rg = tid / CG;
   const int T = a.T;
-  const float* S = a.state + (size_t)bh * D * D;
+  // the stored slice is dk x dv (<= D x D); padded rows and column groups
+  // are zero here and never stored
+  const int dk = a.dk, dv = a.dv;
+  const bool col_ok = 4 * cg < dv;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(a.state + (size_t)bh * dk * dv, dk * dv * 4);
 
   float4 s[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i)
-    s[i] = *reinterpret_cast<const float4*>(S + (size_t)(rg + RG * i) * D +
-                                            4 * cg);
+  for (int i = 0; i < RPT; ++i) {
+    const int c = rg + RG * i;
+    s[i] = __builtin_bit_cast(
+        float4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, (c < dk && col_ok) ? (uint32_t)((c * dv + 4 * cg) * 4)
+                                           : kOffNone, 0, 0));
+  }
 
   // token t of sequence b, head h: row (b * T + t) * H + h
   for (int e = tid; e < T * D; e += NT) {
     const int t = e / D, c = e % D;
     const size_t row = ((size_t)b * T + t) * a.H + h;
-    s_alpha[t][c] = __builtin_amdgcn_exp2f(a.g[row * D + c] * kLog2e);
-    s_k[t][c] = io<Tio>::to_f(static_cast<const Tio*>(a.k)[row * D + c]);
-    s_q[t][c] = io<Tio>::to_f(static_cast<const Tio*>(a.q)[row * D + c]);
+    const bool ok = c < dk;
+    s_alpha[t][c] =
+        ok ? __builtin_amdgcn_exp2f(a.g[row * dk + c] * kLog2e) : 1.f;
+    s_k[t][c] =
+        ok ? io<Tio>::to_f(static_cast<const Tio*>(a.k)[row * dk + c]) : 0.f;
+    s_q[t][c] =
+        ok ? io<Tio>::to_f(static_cast<const Tio*>(a.q)[row * dk + c]) : 0.f;
   }
   __syncthreads();
 
@@ -116,20 +129,25 @@ __global__ __launch_bounds__(NT) void spec_verify_kernel(SpecArgs a) {
       QK += red[r][cg][2].x;
     }
     const size_t row = ((size_t)b * T + t) * a.H + h;
-    const Tio* v = static_cast<const Tio*>(a.v) + row * D + 4 * cg;
+    const Tio* v = static_cast<const Tio*>(a.v) + row * dv + 4 * cg;
     const float beta = a.beta[row];
+    float vv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (col_ok) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[i] = io<Tio>::to_f(v[i]);
+    }
     float4 u;
-    u.x = beta * (io<Tio>::to_f(v[0]) - X.x);
-    u.y = beta * (io<Tio>::to_f(v[1]) - X.y);
-    u.z = beta * (io<Tio>::to_f(v[2]) - X.z);
-    u.w = beta * (io<Tio>::to_f(v[3]) - X.w);
-    if (rg == 0) {
-      Tio* o = static_cast<Tio*>(a.o) + row * D + 4 * cg;
+    u.x = beta * (vv[0] - X.x);
+    u.y = beta * (vv[1] - X.y);
+    u.z = beta * (vv[2] - X.z);
+    u.w = beta * (vv[3] - X.w);
+    if (rg == 0 && col_ok) {
+      Tio* o = static_cast<Tio*>(a.o) + row * dv + 4 * cg;
       o[0] = io<Tio>::from_f(a.scale * (Y.x + QK * u.x));
       o[1] = io<Tio>::from_f(a.scale * (Y.y + QK * u.y));
       o[2] = io<Tio>::from_f(a.scale * (Y.z + QK * u.z));
       o[3] = io<Tio>::from_f(a.scale * (Y.w + QK * u.w));
-      *reinterpret_cast<float4*>(a.u + row * D + 4 * cg) = u;
+      *reinterpret_cast<float4*>(a.u + row * dv + 4 * cg) = u;
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -155,24 +173,34 @@ __global__ __launch_bounds__(NT) void spec_commit_kernel(SpecArgs a) {
   acc = acc < 0 ? 0 : (acc > T ? T : acc);
   if (acc == 0) return;  // uniform: the state stays as it is
 
-  float* S = a.state + (size_t)bh * D * D;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, D * D * 4);
+  const int dk = a.dk, dv = a.dv;
+  const bool col_ok = 4 * cg < dv;
+  float* S = a.state + (size_t)bh * dk * dv;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, dk * dv * 4);
+  auto soff = [&](int c) {
+    return (c < dk && col_ok) ? (uint32_t)((c * dv + 4 * cg) * 4) : kOffNone;
+  };
   float4 s[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
     s[i] = __builtin_bit_cast(
-        float4, __builtin_amdgcn_raw_buffer_load_b128(
-                    rs, ((rg + RG * i) * D + 4 * cg) * 4, 0, kCachePolicyNt));
+        float4, __builtin_amdgcn_raw_buffer_load_b128(rs, soff(rg + RG * i),
+                                                      0, kCachePolicyNt));
   for (int e = tid; e < acc * D; e += NT) {
     const int t = e / D, c = e % D;
     const size_t row = ((size_t)b * T + t) * a.H + h;
-    s_alpha[t][c] = __builtin_amdgcn_exp2f(a.g[row * D + c] * kLog2e);
-    s_k[t][c] = io<Tio>::to_f(static_cast<const Tio*>(a.k)[row * D + c]);
+    const bool ok = c < dk;
+    s_alpha[t][c] =
+        ok ? __builtin_amdgcn_exp2f(a.g[row * dk + c] * kLog2e) : 1.f;
+    s_k[t][c] =
+        ok ? io<Tio>::to_f(static_cast<const Tio*>(a.k)[row * dk + c]) : 0.f;
   }
   __syncthreads();
   for (int t = 0; t < acc; ++t) {
     const size_t row = ((size_t)b * T + t) * a.H + h;
-    const float4 u = *reinterpret_cast<const float4*>(a.u + row * D + 4 * cg);
+    const float4 u =
+        col_ok ? *reinterpret_cast<const float4*>(a.u + row * dv + 4 * cg)
+               : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int c = rg + RG * i;
@@ -185,8 +213,8 @@ __global__ __launch_bounds__(NT) void spec_commit_kernel(SpecArgs a) {
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
     __builtin_amdgcn_raw_buffer_store_b128(
-        __builtin_bit_cast(u32x4, s[i]), rs, ((rg + RG * i) * D + 4 * cg) * 4,
-        0, kCachePolicyNt);
+        __builtin_bit_cast(u32x4, s[i]), rs, soff(rg + RG * i), 0,
+        kCachePolicyNt);
 }
 
 // Threads per workgroup, capped by D^2 / 4.  Commit streams the state like

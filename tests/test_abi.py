@@ -63,7 +63,15 @@ def test_workspace_size_formula():
         (8192 // C + 1) * H * block
     assert kda.kda_prefill_workspace_size(8, 1000, 4, D, D, C) == \
         (1000 // C + 8) * 4 * block
-    assert kda.kda_prefill_workspace_size(1, 10, 1, 96, 96, 64) == 0
+    # any multiple of 16 up to 128, d_k and d_v apart: the blocks are those
+    # of the smallest 16 / 32 / 64 / 128 tile that holds both dims
+    ws = kda.kda_prefill_workspace_size
+    assert ws(1, 8192, H, 96, 96, C) == ws(1, 8192, H, 128, 128, C)
+    assert ws(1, 8192, H, 64, 128, C) == ws(1, 8192, H, 128, 128, C)
+    assert ws(1, 8192, H, 48, 16, C) == ws(1, 8192, H, 64, 64, C)
+    assert ws(1, 10, 1, 100, 100, 64) == 0
+    assert ws(1, 10, 1, 144, 128, 64) == 0
+    assert ws(1, 10, 1, 128, 8, 64) == 0
     assert kda.kda_prefill_workspace_size(1, 10, 1, 128, 128, 48) == 0
     assert kda.kda_prefill_workspace_size(0, 10, 1, 128, 128, 64) == 0
 
@@ -81,8 +89,9 @@ def test_decode_validation():
     lib = kda.load()
     assert _decode(lib, B=0) == INVALID
     assert _decode(lib, H=-1) == INVALID
-    assert _decode(lib, Dk=96, Dv=96) == UNSUP
-    assert _decode(lib, Dk=128, Dv=64) == UNSUP
+    assert _decode(lib, Dk=40, Dv=40) == UNSUP       # not a multiple of 16
+    assert _decode(lib, Dk=144, Dv=128) == UNSUP     # above 128
+    assert _decode(lib, Dk=128, Dv=8) == UNSUP
     assert _decode(lib, dtype=7) == UNSUP
     assert _decode(lib, q=NULL) == INVALID
     assert _decode(lib, state=NULL) == INVALID
@@ -115,6 +124,12 @@ def test_prefill_chunked_validation():
     assert _chunked(lib, ws=NULL) == WS
     assert _chunked(lib, ws_bytes=1000) == WS
     assert _chunked(lib, ws=ctypes.c_void_p(0x100010)) == INVALID
+
+
+def test_head_count_limit_of_32_bit_chunk_buffers():
+    """C + 8 rows of H heads of 128 fp32 channels must stay under 4 GiB."""
+    lib = kda.load()
+    assert _chunked(lib, H=120000) == UNSUP
 
 
 def _varlen(lib, **kw):
@@ -238,7 +253,7 @@ def test_prefill_stage_validation():
     assert _recur(lib, o=NULL) == INVALID
     assert _recur(lib, o=MIS) == INVALID
     assert _recur(lib, s0=MIS) == INVALID
-    assert _recur(lib, Dk=48, Dv=48) == UNSUP
+    assert _recur(lib, Dk=56, Dv=56) == UNSUP
     assert _recur(lib, ws_bytes=10) == WS
 
 
@@ -328,7 +343,7 @@ def test_spec_validation():
     assert _verify(lib, T=0) == INVALID
     assert _verify(lib, T=17) == UNSUP
     assert _verify(lib, B=0) == INVALID
-    assert _verify(lib, Dk=96, Dv=96) == UNSUP
+    assert _verify(lib, Dk=100, Dv=100) == UNSUP
     assert _verify(lib, dtype=5) == UNSUP
     assert _verify(lib, u=NULL) == INVALID
     assert _verify(lib, state=MIS) == INVALID
@@ -339,7 +354,7 @@ def test_spec_validation():
     assert _commit(lib, acc=ctypes.c_void_p(0x100002)) == INVALID
     assert _commit(lib, state=NULL) == INVALID
     assert _commit(lib, u=MIS) == INVALID
-    assert _commit(lib, Dk=64, Dv=128) == UNSUP
+    assert _commit(lib, Dk=64, Dv=136) == UNSUP
 
 
 def _epi(lib, **kw):
@@ -358,7 +373,7 @@ def test_epilogue_validation():
     assert _epi(lib, H=0) == INVALID
     assert _epi(lib, eps=-1.0) == INVALID
     assert _epi(lib, eps=float("nan")) == INVALID
-    assert _epi(lib, Dv=96) == UNSUP
+    assert _epi(lib, Dv=72) == UNSUP
     assert _epi(lib, dtype=9) == UNSUP
     assert _epi(lib, z=NULL) == INVALID
     assert _epi(lib, w=MIS) == INVALID
@@ -390,5 +405,9 @@ def test_prologue_validation():
     assert call(w=ctypes.c_void_p(0x100004)) == INVALID
     assert call(N=0) == INVALID
     assert call(a=NULL) == INVALID
-    assert call(D=96) == UNSUP
+    assert call(D=100) == UNSUP
     assert call(ws_bytes=100) == WS
+    # the short convolution's taps are per channel of q, k and v: Dk == Dv
+    assert lib.kda_prefill_varlen_prologue(
+        P, P, P, P, P, P, P, 2, 100, 64, NULL, NULL, P, 2, 64, 128, 64, 1.0,
+        0, P, 1 << 40, NULL) == UNSUP
