@@ -53,7 +53,7 @@ template <> struct Vec4<float> {
 
 constexpr int kEpiThreads = 256;
 
-template <typename Tio, int D>
+template <typename Tio, int D, bool kExact>
 __global__ __launch_bounds__(kEpiThreads) void norm_gate_kernel(EpilogueArgs a) {
   constexpr int LPR = D / 4;                 // lanes per row
   constexpr int RPB = kEpiThreads / LPR;     // rows per workgroup
@@ -66,7 +66,8 @@ __global__ __launch_bounds__(kEpiThreads) void norm_gate_kernel(EpilogueArgs a) 
   const int64_t first = (int64_t)blockIdx.x * RPB;
   const int64_t nrows = a.rows - first < RPB ? a.rows - first : RPB;
   // rows hold dv <= D channels; lanes past them read 0 and store nothing
-  const int dv = a.dv;
+  // (kExact: dv = D at compile time)
+  const int dv = kExact ? D : a.dv;
   const bool col_ok = 4 * lr < dv;
   const uint32_t bytes = (uint32_t)(nrows * dv * sizeof(Tio));
   const __amdgpu_buffer_rsrc_t ro =
@@ -100,8 +101,11 @@ template <typename Tio, int D>
 hipError_t launch_d(const EpilogueArgs& a, hipStream_t st) {
   constexpr int RPB = kEpiThreads / (D / 4);
   const int64_t blocks = (a.rows + RPB - 1) / RPB;
-  return launch_kernel(norm_gate_kernel<Tio, D>, dim3((unsigned)blocks),
-                       dim3(kEpiThreads), st, a);
+  return a.dv == D
+             ? launch_kernel(norm_gate_kernel<Tio, D, true>,
+                             dim3((unsigned)blocks), dim3(kEpiThreads), st, a)
+             : launch_kernel(norm_gate_kernel<Tio, D, false>,
+                             dim3((unsigned)blocks), dim3(kEpiThreads), st, a);
 }
 
 template <typename Tio>
