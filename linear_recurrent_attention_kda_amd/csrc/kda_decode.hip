@@ -202,8 +202,9 @@ void decode_kernel(DecodeArgs a) {
 
 // Launch shape: one float4 per thread and row group, at most 1024 threads
 // per workgroup (D^2 / 4 below D = 64).  At D = 128, 1024 threads hold 4 rows
-// each in 60 VGPRs, so two workgroups (128 KB of state loads) are in flight
-// per CU.  The state is touched once per step, so its accesses carry the
+// each in 44 VGPRs (46 with the fused output epilogue, 50-53 in the
+// run-time-stride variants), so two workgroups (128 KB of state loads) are
+// in flight per CU.  The state is touched once per step, so its accesses carry the
 // non-temporal policy (measured: the kernel's own time then covers all of
 // its traffic, and back-to-back steps run at the streaming ceiling).
 // Head dims equal to the tile run a variant with compile-time strides
