@@ -298,6 +298,12 @@ def main(argv=None):
         prep_ms = [a.elapsed_time(m) for a, m, _, _ in rec]
         recur_ms = [m.elapsed_time(b) for _, m, b, _ in rec]
     ms_step = wall * 1e3 / args.steps
+
+    def busy():  # whole steps (prefill and decode), then wait
+        for i in range(3):
+            step(i)
+        torch.cuda.synchronize()
+    clocks = gpu_clocks(busy)  # clocks under load, after the timed steps
     pre_avg = float(np.mean(pre_ms))
     dec_avg = float(np.mean(dec_ms))
     pre_med = float(np.median(pre_ms))
@@ -397,6 +403,25 @@ def main(argv=None):
     kernels.append(dec_entry)
     # the roofline line is the kernel that takes the largest share of a step
     dominant = max(kernels, key=lambda e: e["avg_launch_ms"])
+    # The prefill's place under the roofline by the pages' FLOP count, with
+    # the arithmetic intensity taken over the bytes the HBM counters read for
+    # its two kernels (when they are current): achieved FLOP/s over
+    # min(MFMA peak, intensity x HBM peak).
+    pre_traffic = None
+    if len(kernels) == 3 and all(e.get("traffic") for e in kernels[:2]):
+        pre_traffic = sum(e["traffic"] for e in kernels[:2])
+    pages_roof = None
+    if pre_traffic:
+        ai = pre_flops / pre_traffic
+        bound = min(counts.BF16_MFMA_PEAK_TFLOPS,
+                    ai * counts.HBM_PEAK_GBPS / 1e3)
+        pages_roof = {
+            "counter_bytes": int(pre_traffic),
+            "ai_flop_per_byte": round(ai, 2),
+            "bound_tflops": round(bound, 1),
+            "achieved_tflops": round(pre_flops / pre_s / 1e12, 2),
+            "frac": round(pre_flops / pre_s / 1e12 / bound, 4),
+        }
 
     result = {
         "metric": METRIC,
@@ -451,7 +476,9 @@ def main(argv=None):
                 "minimal_bytes_frac": round(pre_bytes_min / pre_s / 1e9 /
                                             counts.HBM_PEAK_GBPS, 4),
             },
+            "pages_roofline": pages_roof,
         },
+        "gpu_clocks": clocks,
     }
 
     if spec is not None:
@@ -466,9 +493,83 @@ def main(argv=None):
 
     # ---------------- CPU baseline: the oracle on the host cores -----------
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(dp, pp, samples)
+        cb = cpu_baseline(dp, pp, samples)
+        # the GPU's rate over the oracle's on the same workloads
+        sp = {"decode": round(dec_gbps / cb["value"], 1),
+              "prefill": round(total / pre_s / cb["prefill_tokens_per_s"], 1)}
+        for name, leg in (legs or {}).items():
+            cw = cb.get("workloads", {}).get(name, {})
+            if "tokens_per_s" in leg and cw.get("tokens_per_s"):
+                sp[name] = round(leg["tokens_per_s"] / cw["tokens_per_s"], 1)
+        cb["gpu_over_cpu"] = sp
+        result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
     return 0
+
+
+def _clock_entries(node, path=""):
+    """(path, value) leaves of an SMI JSON report whose path names a clock."""
+    out = []
+    if isinstance(node, dict):
+        for k, v in node.items():
+            out += _clock_entries(v, path + "/" + str(k))
+    elif isinstance(node, list):
+        for i, v in enumerate(node):
+            out += _clock_entries(v, path + "/" + str(i))
+    elif ("clk" in path.lower() or "clock" in path.lower()) and \
+            isinstance(node, (int, float, str)):
+        out.append((path.strip("/"), node))
+    return out
+
+
+def gpu_clocks(busy=None):
+    """The GPU's clocks as the driver reports them (amd-smi, else rocm-smi:
+    read-only queries, nothing is pinned or changed), read while `busy()`
+    keeps the GPU working, so that the figures are the loaded clocks rather
+    than idle ones.  Returns the current gfx clock of each XCD, the memory
+    clock, the gfx maximum and whether clocks are locked; the raw text when
+    the report is not JSON; or None."""
+    import subprocess
+    for cmd in (["amd-smi", "metric", "-g", "0", "-c", "--json"],
+                ["rocm-smi", "-d", "0", "--showclocks", "--json"]):
+        try:
+            proc = subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                    stderr=subprocess.DEVNULL, text=True)
+        except OSError:
+            continue
+        t0 = time.perf_counter()
+        while proc.poll() is None and time.perf_counter() - t0 < 20:
+            if busy is not None:
+                busy()
+            else:
+                time.sleep(0.05)
+        if proc.poll() is None:
+            proc.kill()
+            proc.wait()
+            continue
+        text = proc.stdout.read()
+        if proc.returncode != 0 or not text.strip():
+            continue
+        try:
+            found = _clock_entries(json.loads(text))
+        except ValueError:
+            return {"tool": cmd[0], "raw": text.strip()[:600]}
+        gfx = [v for k, v in found
+               if "/gfx_" in k and k.endswith("/clk/value")]
+        mem = [v for k, v in found
+               if "/mem_" in k and k.endswith("/clk/value")]
+        gmax = [v for k, v in found
+                if "/gfx_" in k and k.endswith("/max_clk/value")]
+        locked = sorted({str(v) for k, v in found if k.endswith("clk_locked")})
+        if not gfx:
+            return {"tool": cmd[0], "clocks": dict(found[:40])}
+        return {"tool": cmd[0], "gfx_reported_mhz": gfx, "mem_mhz": mem,
+                "gfx_max_mhz": max(gmax) if gmax else None,
+                "clk_locked": locked,
+                "read": "while whole steps run; gfx_reported_mhz is the "
+                        "driver's sampled figure (it has read 158 to 2,400 "
+                        "MHz under the same load), not the kernels' clock"}
+    return None
 
 
 def time_tiny(dev, stream, ev):
