@@ -33,7 +33,12 @@ def make_case(seed, lengths, H, D, C, dtype="bf16", s0=True):
                 C=C, dtype=dtype, lengths=list(lengths))
 
 
-def check(c, label):
+def check(c, label, rounded_ref=False):
+    """GPU prologue-fused prefill against the oracle prologue followed by the
+    oracle recurrence.  With rounded_ref, the prologue's q, k and v are first
+    rounded to the storage dtype, as the kernel rounds them before the chunk
+    stages (the reference then differs from the kernel by the kernels'
+    arithmetic only; the unrounded comparison is logged beside it)."""
     U.log("prologue", label, "H=%d D=%d C=%d %s lengths=%s"
           % (c["H"], c["D"], c["C"], c["dtype"], c["lengths"]))
     dev = lambda x: U.to_dev(x, c["dtype"])  # noqa: E731
@@ -49,6 +54,15 @@ def check(c, label):
     eo = max(U.prefill_o_rel(U.host(o), o_ref, c["cu"], c["C"]))
     es = U.slice_rel(U.host(s), s_ref, (0, 1))
     U.log("   o rel err %.3e   final state rel err %.3e" % (eo, es))
+    if rounded_ref and c["dtype"] == "bf16":
+        rnd = lambda x: inputs.bf16_round(  # noqa: E731
+            np.asarray(x, np.float32)).astype(np.float64)
+        o_ref, s_ref = oracle.run_varlen(rnd(q), rnd(k), rnd(v), g, beta,
+                                         c["cu"], c["S0"])
+        eo = max(U.prefill_o_rel(U.host(o), o_ref, c["cu"], c["C"]))
+        es = U.slice_rel(U.host(s), s_ref, (0, 1))
+        U.log("   against q, k, v rounded to bf16 as stored: o rel err "
+              "%.3e   final state rel err %.3e" % (eo, es))
     assert eo <= U.PREFILL_TOL and es <= U.PREFILL_TOL
 
 

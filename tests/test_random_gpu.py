@@ -72,3 +72,118 @@ def test_random_prefill_and_decode(seed):
     d = inputs.make("decode", seed=seed, B=3, H=p.H, K=p.K, V=p.V,
                     dtype=p.dtype)
     U.check_decode(d, scale=scale)
+
+
+def as_varlen(c):
+    """The packed form of a drawn case (fixed-length batches become B
+    sequences of T tokens)."""
+    c = dict(c)
+    if c.pop("kind") == "prefill":
+        c["lengths"] = [c.pop("T")] * c.pop("B")
+    return c
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_gated_prefill(seed):
+    """kda_prefill_varlen_gated on random mixes: the fused kernel where the
+    draw gives at least two (sequence, head) pairs per compute unit, the
+    two-pass path otherwise (test_prefill_gated_gpu's two measures)."""
+    import test_prefill_gated_gpu as G
+    c, _ = draw(100 + seed)
+    c = as_varlen(c)
+    if seed % 4 == 0:  # enough pairs for the fused kernel (130 x 4 >= 512)
+        c["H"] = 130
+        c["lengths"] = (c["lengths"] + [17, 64, 1, 40])[:max(4, len(c["lengths"]))]
+    p = inputs.make("varlen", seed=100 + seed, **c)
+    G.check_gated(p, 100 + seed, "random case %d" % seed,
+                  head_group=48 if p.H > 48 else None)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_ckpt_positions(seed):
+    """kda_prefill_varlen_ckpt_at with random position lists per sequence
+    (chunk edges and the sequence's own length, some lists empty)."""
+    import test_ckpt_gpu as CK
+    c, _ = draw(200 + seed)
+    c = as_varlen(c)
+    p = inputs.make("varlen", seed=200 + seed, **c)
+    rng = np.random.default_rng(300 + seed)
+    C = p.C
+    positions = []
+    for L in p.seq_lengths.tolist():
+        cand = sorted(set(list(range(C, L + 1, C)) + ([L] if L > 0 else [])))
+        k = int(rng.integers(0, 4))
+        pick = rng.choice(cand, size=min(k, len(cand)), replace=False) \
+            if cand else []
+        positions.append(sorted(int(x) for x in pick))
+    n = CK.check_ckpt_at(p, positions, label="random case %d" % seed,
+                         head_group=48 if p.H > 48 else None)
+    assert n == sum(len(x) for x in positions)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_spec_verify_commit(seed):
+    """Draft verify of T <= 16 tokens from cached states, then commit of a
+    random accepted prefix per sequence (0 .. T, and one count past T, which
+    is clamped), on random head dims."""
+    import torch
+    import oracle
+    from linear_recurrent_attention_kda_amd import kda
+    rng = np.random.default_rng(400 + seed)
+    dims = [16 * i for i in range(1, 9)]
+    Dk, Dv = int(rng.choice(dims)), int(rng.choice(dims))
+    B, T = int(rng.integers(1, 9)), int(rng.integers(1, 17))
+    H = int(rng.choice([1, 2, 5, 33]))
+    dtype = "bf16" if rng.random() < 0.75 else "fp32"
+    p = inputs.make("varlen", seed=400 + seed, H=H, K=Dk, V=Dv, dtype=dtype,
+                    lengths=[T] * B)
+    accepted = [int(a) for a in rng.integers(0, T + 1, size=B)]
+    accepted[0] = T + 3
+    U.log("random spec case %d: B=%d T=%d H=%d Dk=%d Dv=%d %s accepted=%s"
+          % (seed, B, T, H, Dk, Dv, dtype, accepted))
+    shp = lambda x: x.reshape((B, T) + x.shape[1:])  # noqa: E731
+    q, k, v = (U.to_dev(shp(x), p.dtype) for x in (p.q, p.k, p.v))
+    g, beta = U.f32_dev(shp(p.g)), U.f32_dev(shp(p.beta))
+    state = U.f32_dev(p.initial_state)
+    o, u = kda.kda_spec_verify(q, k, v, g, beta, state)
+    kda.kda_spec_commit(k, g, u, torch.tensor(accepted, dtype=torch.int32,
+                                              device=U.DEV), state)
+    torch.cuda.synchronize()
+    o_ref, _ = oracle.run_varlen(p.q, p.k, p.v, p.g, p.beta, p.cu_seqlens,
+                                 p.initial_state)
+    eo = U.slice_rel(U.host(o).reshape(B * T, H, Dv), o_ref, (1,))
+    s_ref = np.array(p.initial_state, np.float64)
+    for b, a in enumerate(min(a, T) for a in accepted):
+        if a:
+            lo = b * T
+            _, s = oracle.run_varlen(p.q[lo:lo + a], p.k[lo:lo + a],
+                                     p.v[lo:lo + a], p.g[lo:lo + a],
+                                     p.beta[lo:lo + a], np.array([0, a]),
+                                     p.initial_state[b:b + 1],
+                                     want_output=False)
+            s_ref[b] = s[0]
+    es = U.slice_rel(U.host(state), s_ref, (0, 1))
+    U.log("   o rel err %.3e   committed state rel err %.3e" % (eo, es))
+    assert eo <= U.DECODE_O_TOL[dtype] and es <= U.DECODE_STATE_TOL
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_prologue(seed):
+    """kda_prefill_varlen_prologue (d_k = d_v) on random sizes and lengths.
+    The kernel rounds the prologue's q, k and v to the storage dtype before
+    the chunk stages, as stored inputs would be; the reference applies the
+    same rounding (the unrounded comparison is logged).  Without it a call
+    holding only a 2-token sequence from a zero state (case 4: q . k down to
+    0.004) is off by 2.2e-2 from the rounding of its inputs alone."""
+    import test_prologue_gpu as PR
+    rng = np.random.default_rng(600 + seed)
+    D = int(rng.choice([16 * i for i in range(1, 9)]))
+    C = int(rng.choice([16, 32, 64]))
+    H = int(rng.choice([1, 3, 33, 70]))
+    n = int(rng.integers(1, 6))
+    lengths = [int(x) for x in rng.integers(0, 200, size=n)]
+    lengths[int(rng.integers(0, n))] = int(rng.integers(1, 200))
+    dtype = "bf16" if rng.random() < 0.75 else "fp32"
+    s0 = bool(rng.random() < 0.7)
+    PR.check(PR.make_case(600 + seed, lengths, H, D, C, dtype, s0),
+             "random case %d" % seed, rounded_ref=True)
