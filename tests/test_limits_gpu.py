@@ -111,3 +111,42 @@ def test_inputs_beyond_4_gib():
         es = U.slice_rel(U.host(s[:, [dev_head]]), s_ref, (0, 1))
         U.log("   head %d: o rel %.3e state rel %.3e" % (dev_head, eo, es))
         assert eo <= U.PREFILL_TOL and es <= U.PREFILL_TOL
+
+
+def test_head_count_at_the_offset_limit():
+    """116,480 heads of fp32 at d = 128, C = 64: a chunk's token rows plus
+    the prologue's halo, (C + 8) * H * 128 * 4 bytes, come within 1 MB of the
+    4 GiB that the kernels' 32-bit buffer offsets allow (the largest head
+    count the library accepts at this size is 116,508).  An 8-head block is
+    drawn and repeated along the heads on the device; every repeat must equal
+    the first bit for bit (so the heads at the top of the offset range are
+    addressed like the first ones), and the first block must match the
+    oracle.  T = 130 ends in a partial chunk.  About 80 GB of device memory."""
+    base = inputs.make("prefill", seed=56, B=1, T=130, H=8, dtype="fp32",
+                       s0=True)
+    rh = 14560
+    H = base.H * rh
+    assert (base.C + 8) * H * 128 * 4 <= 0xFFFF0000
+    U.log("prefill at the offset limit: T=%d H=%d fp32" % (base.T, H))
+
+    def tiled(x):
+        t = U.f32_dev(x)
+        return t.repeat((1, 1, rh) + (1,) * (t.dim() - 3))
+
+    q, k, v, g = (tiled(x) for x in (base.q, base.k, base.v, base.g))
+    beta = tiled(base.beta)
+    s0 = U.f32_dev(base.initial_state).repeat(1, rh, 1, 1)
+    o, s = kda.kda_prefill_chunked(q, k, v, g, beta, s0, chunk_size=base.C)
+    torch.cuda.synchronize()
+    del q, k, v, g, beta, s0
+    h0 = base.H
+    for j in (1, rh // 2, rh - 1):
+        assert torch.equal(o[:, :, :h0], o[:, :, j * h0:(j + 1) * h0]), j
+        assert torch.equal(s[:, :h0], s[:, j * h0:(j + 1) * h0]), j
+    o_ref, s_ref = oracle.run_fixed(base.q, base.k, base.v, base.g,
+                                    base.beta, base.initial_state)
+    eo = max(U.prefill_o_rel(U.host(o[:, :, :h0]), o_ref, [0, base.T],
+                             base.C))
+    es = U.slice_rel(U.host(s[:, :h0]), s_ref, (0, 1))
+    U.log("   first block: o rel %.3e state rel %.3e" % (eo, es))
+    assert eo <= U.PREFILL_TOL and es <= U.PREFILL_TOL
