@@ -319,7 +319,7 @@ def main(argv=None):
     # sustained case of a decode-only server loop
     n_b2b, b2b_ms, copy_ref = 0, None, None
     if not args.step_only:
-        n_b2b = max(3 * args.steps, 30)
+        n_b2b = max(5 * args.steps, 100)  # >= 100 decode iterations
         for i in range(6):
             decode(i)
         b0, b1 = ev(), ev()
