@@ -304,6 +304,18 @@ def main(argv=None):
             step(i)
         torch.cuda.synchronize()
     clocks = gpu_clocks(busy)  # clocks under load, after the timed steps
+
+    # the results of the step's prefill (po, pfs: the same every step) and
+    # of one decode step from the initial state, for the oracle leg's
+    # parity figures
+    gpu_res = None
+    if not args.no_cpu_baseline:
+        st1 = torch.from_numpy(np.ascontiguousarray(dp.initial_state)).to(dev)
+        o1 = kda.kda_decode_step(dq, dk, dv, dg, dbeta, st1)
+        torch.cuda.synchronize()
+        gpu_res = {"prefill": (po.float().cpu().numpy(), pfs.cpu().numpy()),
+                   "decode": (o1.float().cpu().numpy(), st1.cpu().numpy())}
+        del st1, o1
     pre_avg = float(np.mean(pre_ms))
     dec_avg = float(np.mean(dec_ms))
     pre_med = float(np.median(pre_ms))
@@ -493,7 +505,7 @@ def main(argv=None):
 
     # ---------------- CPU baseline: the oracle on the host cores -----------
     if not args.no_cpu_baseline:
-        cb = cpu_baseline(dp, pp, samples)
+        cb = cpu_baseline(dp, pp, samples, gpu_res)
         # the GPU's rate over the oracle's on the same workloads
         sp = {"decode": round(dec_gbps / cb["value"], 1),
               "prefill": round(total / pre_s / cb["prefill_tokens_per_s"], 1)}
@@ -692,7 +704,10 @@ def time_prefill_workload(name, dev, stream, ev, reps=5):
                   s0=None if w["initial_state"] is None else
                   w["initial_state"][:, :nh].cpu().numpy(),
                   cu=w["cu_seqlens"].cpu().numpy(), heads=nh, H=H,
-                  total=total)
+                  total=total, C=C,
+                  # the plain prefill's results on those heads, for the
+                  # oracle leg's parity figures
+                  o_gpu=host(o), fs_gpu=fs[:, :nh].cpu().numpy())
     del w, o, fs, ws
     torch.cuda.empty_cache()
     return leg, sample
@@ -912,7 +927,27 @@ def host_cpus() -> int:
         return os.cpu_count() or 1
 
 
-def cpu_baseline(dp, pp, samples=None):
+def _rel_per_slice(x, ref, cu=None):
+    """Largest max|x - ref| / max|ref| over the (sequence, head) slices of
+    [tokens, heads, d] outputs (cu: sequence bounds) or over the leading two
+    axes of [sequences, heads, ...] states and decode outputs (cu None)."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if cu is None:
+        ax = tuple(range(2, x.ndim))
+        num = np.max(np.abs(x - ref), axis=ax)
+        den = np.maximum(np.max(np.abs(ref), axis=ax), 1e-30)
+        return float(np.max(num / den)) if num.size else 0.0
+    worst = 0.0
+    for b, e in zip(cu[:-1], cu[1:]):
+        if e > b:
+            num = np.max(np.abs(x[b:e] - ref[b:e]), axis=(0, 2))
+            den = np.maximum(np.max(np.abs(ref[b:e]), axis=(0, 2)), 1e-30)
+            worst = max(worst, float(np.max(num / den)))
+    return worst
+
+
+def cpu_baseline(dp, pp, samples=None, gpu=None):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
     workloads: the whole decode step, the prefill over a head sample of all
     of its tokens (scaled to all heads), and the same for the other
@@ -924,9 +959,19 @@ def cpu_baseline(dp, pp, samples=None):
     oracle.set_threads(threads)
     # each leg repeats (same inputs, results discarded) until it has run
     # for a few seconds, so that the rate is not one short noisy sample
+    # The first run of each leg also gives the parity figures: the GPU's
+    # results on the same inputs against the oracle's, per (sequence, head),
+    # as the tests measure them (bars: 2e-2 for prefill outputs and states,
+    # 1e-4 for the fp32 decode state).
+    gpu = gpu or {}
+    parity = {}
     dec_reps, t = 0, time.perf_counter()
     while dec_reps == 0 or time.perf_counter() - t < 4.0:
-        oracle.run_decode(dp.q, dp.k, dp.v, dp.g, dp.beta, dp.initial_state)
+        r = oracle.run_decode(dp.q, dp.k, dp.v, dp.g, dp.beta,
+                              dp.initial_state)
+        if dec_reps == 0 and "decode" in gpu:
+            parity["decode_o"] = _rel_per_slice(gpu["decode"][0], r[0])
+            parity["decode_state"] = _rel_per_slice(gpu["decode"][1], r[1])
         dec_reps += 1
     dec_s = (time.perf_counter() - t) / dec_reps
     dec_bytes = counts.decode_bytes_per_head(dp.K) * dp.B * dp.H
@@ -941,11 +986,19 @@ def cpu_baseline(dp, pp, samples=None):
     pre_reps, t = 0, time.perf_counter()
     while pre_reps == 0 or time.perf_counter() - t < 6.0:
         if pp.kind == "varlen":
-            oracle.run_varlen(sel(pp.q), sel(pp.k), sel(pp.v), sel(pp.g),
-                              pp.beta[..., heads], pp.cu_seqlens, s0)
+            r = oracle.run_varlen(sel(pp.q), sel(pp.k), sel(pp.v), sel(pp.g),
+                                  pp.beta[..., heads], pp.cu_seqlens, s0)
         else:
-            oracle.run_fixed(sel(pp.q), sel(pp.k), sel(pp.v), sel(pp.g),
-                             pp.beta[..., heads], s0)
+            r = oracle.run_fixed(sel(pp.q), sel(pp.k), sel(pp.v), sel(pp.g),
+                                 pp.beta[..., heads], s0)
+        if pre_reps == 0 and "prefill" in gpu:
+            go, gs = gpu["prefill"]
+            cu = (pp.cu_seqlens if pp.kind == "varlen" else
+                  np.arange(pp.B + 1) * pp.T)
+            ref_o = np.asarray(r[0]).reshape((-1,) + r[0].shape[-2:])
+            parity["prefill_o"] = _rel_per_slice(
+                go.reshape((-1,) + go.shape[-2:])[:, heads], ref_o, cu)
+            parity["prefill_state"] = _rel_per_slice(gs[:, heads], r[1])
         pre_reps += 1
     pre_s = (time.perf_counter() - t) / pre_reps
     total = int(pp.cu_seqlens[-1]) if pp.kind == "varlen" else pp.B * pp.T
@@ -956,8 +1009,12 @@ def cpu_baseline(dp, pp, samples=None):
     for name, smp in (samples or {}).items():
         reps, t = 0, time.perf_counter()
         while reps == 0 or time.perf_counter() - t < 2.0:
-            oracle.run_varlen(smp["q"], smp["k"], smp["v"], smp["g"],
-                              smp["beta"], smp["cu"], smp["s0"])
+            r = oracle.run_varlen(smp["q"], smp["k"], smp["v"], smp["g"],
+                                  smp["beta"], smp["cu"], smp["s0"])
+            if reps == 0 and "o_gpu" in smp:
+                parity[name + "_o"] = _rel_per_slice(smp["o_gpu"], r[0],
+                                                     smp["cu"])
+                parity[name + "_state"] = _rel_per_slice(smp["fs_gpu"], r[1])
             reps += 1
         sec = (time.perf_counter() - t) / reps
         legs[name] = {
@@ -983,6 +1040,7 @@ def cpu_baseline(dp, pp, samples=None):
         "host_cpus": os.cpu_count(),
         "affinity_cpus": host_cpus(),
         "kind": "oracle",
+        "parity": {k: float("%.3e" % v) for k, v in parity.items()},
         "sample": "whole decode step (%dx%d heads, d=%d) in fp64, mean of "
                   "%d runs; prefill: %d of %d heads over all %d tokens, "
                   "scaled to all heads, mean of %d runs"

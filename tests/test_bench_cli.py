@@ -55,3 +55,27 @@ def test_stored_mfma_counts_equal_the_kernels_products():
     assert float(_stored("mfma", "kda_recur")["bf16_mops"]) * 512 == \
         recur * units
     assert float(_stored("mfma", "kda_decode")["bf16_mops"]) == 0.0
+
+
+def test_parity_figure_is_the_worst_sequence_head_slice():
+    """The oracle leg's parity figure: per (sequence, head) slice, the
+    largest absolute error over the slice's largest reference magnitude,
+    maximised over slices.  One slice scaled by 1.01 reads 1e-2, whether
+    the layout is packed tokens (with sequence bounds) or states."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import bench
+    ref = np.random.default_rng(0).standard_normal((100, 3, 8))
+    x = ref.copy()
+    x[10:20, 1] *= 1.01          # inside sequence 0, head 1
+    assert abs(bench._rel_per_slice(x, ref, np.array([0, 50, 100]))
+               - 0.01) < 1e-12
+    # the same rows measured as their own sequence: the whole slice is off
+    # by 1 %, the other sequences not at all
+    assert abs(bench._rel_per_slice(x, ref, np.array([0, 10, 20, 100]))
+               - 0.01) < 1e-12
+    assert bench._rel_per_slice(ref, ref, np.array([0, 0, 100])) == 0.0
+    s = ref.reshape(4, 25, 3, 8).transpose(0, 2, 1, 3)   # [seq, head, ...]
+    t = s.copy()
+    t[2, 0] += 0.5 * np.abs(s[2, 0]).max()
+    assert abs(bench._rel_per_slice(t, s) - 0.5) < 1e-12
