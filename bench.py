@@ -715,7 +715,9 @@ def time_prefill_workload(name, dev, stream, ev, reps=5):
 
 def time_spec(T, dp, states, dev, stream, ev):
     """Speculative verify of T draft tokens per sequence on the decode
-    batch, then commit of all T, against T single decode steps."""
+    batch, then commit of all T, against T single decode steps; and the
+    fused step (commit of a previous T-token draft, all accepted, then
+    verify of the next) against the two calls."""
     import torch
     from linear_recurrent_attention_kda_amd import kda
     sp = inputs.make("varlen", seed=5, H=dp.H, K=dp.K, V=dp.V,
@@ -756,9 +758,13 @@ def time_spec(T, dp, states, dev, stream, ev):
             kda.kda_decode_step(qs[t], ks[t], vs[t], gs[t], bs[t],
                                 states[i % 3], o=od)
     dec = timed(steps)
+    o2, u2 = torch.empty_like(o), torch.empty_like(u)
+    stp = timed(lambda i: kda.kda_spec_step(
+        q, k, v, g, beta, states[i % 3], k_prev=k, g_prev=g, u_prev=u,
+        accepted_prev=acc, o=o2, u=u2))
     per_head = dp.K * dp.V * 4
-    log("spec T=%d: verify %.4f ms, commit %.4f ms, %d decode steps %.4f ms"
-        % (T, ver, com, T, dec))
+    log("spec T=%d: verify %.4f ms, commit %.4f ms, %d decode steps %.4f ms, "
+        "fused step %.4f ms" % (T, ver, com, T, dec, stp))
     return {
         "draft_tokens": T, "sequences": B, "heads": H,
         "verify_ms": round(ver, 5), "commit_ms": round(com, 5),
@@ -768,6 +774,10 @@ def time_spec(T, dp, states, dev, stream, ev):
         "commit_state_gbps": round(2 * B * H * per_head / (com * 1e-3) / 1e9,
                                    1),
         "speedup_vs_decode_steps": round(dec / (ver + com), 3),
+        "step_ms": round(stp, 5),
+        "step_state_gbps": round(2 * B * H * per_head / (stp * 1e-3) / 1e9,
+                                 1),
+        "step_speedup_vs_verify_commit": round((ver + com) / stp, 3),
     }
 
 

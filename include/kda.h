@@ -427,6 +427,35 @@ kda_status_t kda_spec_commit(const void* k, const float* g, const float* u,
                              int32_t T, int32_t H, int32_t Dk, int32_t Dv,
                              int32_t dtype, void* stream);
 
+/*
+ * One speculative-decode step in a single pass over the state (same source
+ * and section as kda_spec_verify): the previous draft's accepted prefix is
+ * applied to `state` and written back (as kda_spec_commit), then the new
+ * draft is verified from the updated state (as kda_spec_verify).  The two
+ * calls read the state twice and write it once; this reads and writes it
+ * once.  Results (state, o, u) equal kda_spec_commit followed by
+ * kda_spec_verify bit for bit.
+ *   k_prev [B, T_prev, H, Dk] dtype, g_prev [B, T_prev, H, Dk] fp32 and
+ *   u_prev [B, T_prev, H, Dv] fp32: the previous draft's k, g and the u
+ *   its verify (or step) wrote; accepted_prev: DEVICE int32 [B], clamped to
+ *   [0, T_prev] (0: that sequence's state is neither changed nor written).
+ *   T_prev = 0 means no previous draft: the four pointers are ignored (may
+ *   be NULL) and the call is kda_spec_verify on `state`.
+ *   state [B, H, Dk, Dv] fp32, updated in place by the commit only.
+ *   u may be the very buffer u_prev when T == T_prev (each workgroup reads
+ *   its previous rows before writing its new ones); any other overlap of u
+ *   with u_prev, or with the inputs, is not allowed.  u == u_prev with
+ *   T != T_prev returns KDA_ERR_INVALID_ARG.
+ * Other arguments as kda_spec_verify; 0 <= T_prev <= 16.
+ */
+kda_status_t kda_spec_step(const void* k_prev, const float* g_prev,
+                           const float* u_prev, const int32_t* accepted_prev,
+                           int32_t T_prev, const void* q, const void* k,
+                           const void* v, const float* g, const float* beta,
+                           float* state, void* o, float* u, int32_t B,
+                           int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                           float scale, int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -579,7 +579,8 @@ kda_status_t kda_spec_verify(const void* q, const void* k, const void* v,
   a.B = B; a.T = T; a.H = H;
   a.dk = Dk; a.dv = Dv;
   a.scale = scale;
-  if (kda::launch_spec(a, tile_dim(Dk, Dv), dtype == KDA_DTYPE_BF16, false,
+  if (kda::launch_spec(a, tile_dim(Dk, Dv), dtype == KDA_DTYPE_BF16,
+                       kda::SpecMode::kVerify,
                        static_cast<hipStream_t>(stream)) != hipSuccess)
     return KDA_ERR_LAUNCH;
   return KDA_OK;
@@ -607,7 +608,57 @@ kda_status_t kda_spec_commit(const void* k, const float* g, const float* u,
   a.state = state;
   a.B = B; a.T = T; a.H = H;
   a.dk = Dk; a.dv = Dv;
-  if (kda::launch_spec(a, tile_dim(Dk, Dv), dtype == KDA_DTYPE_BF16, true,
+  if (kda::launch_spec(a, tile_dim(Dk, Dv), dtype == KDA_DTYPE_BF16,
+                       kda::SpecMode::kCommit,
+                       static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KDA_ERR_LAUNCH;
+  return KDA_OK;
+}
+
+kda_status_t kda_spec_step(const void* k_prev, const float* g_prev,
+                           const float* u_prev, const int32_t* accepted_prev,
+                           int32_t T_prev, const void* q, const void* k,
+                           const void* v, const float* g, const float* beta,
+                           float* state, void* o, float* u, int32_t B,
+                           int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                           float scale, int32_t dtype, void* stream) {
+  if (B <= 0 || H <= 0 || T <= 0 || Dk <= 0 || Dv <= 0 || T_prev < 0)
+    return KDA_ERR_INVALID_ARG;
+  if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_FP32)
+    return KDA_ERR_UNSUPPORTED;
+  if (!supported_dims(Dk, Dv) || T > kda::max_spec_tokens() ||
+      T_prev > kda::max_spec_tokens())
+    return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > INT_MAX) return KDA_ERR_UNSUPPORTED;
+  kda_status_t st = check_tensors((int64_t)B * T, q, k, v, g, beta, o);
+  if (st != KDA_OK) return st;
+  if (!state || !aligned(state, 16) || !u || !aligned(u, 16))
+    return KDA_ERR_INVALID_ARG;
+  if (T_prev > 0) {
+    if (!k_prev || !g_prev || !u_prev || !accepted_prev)
+      return KDA_ERR_INVALID_ARG;
+    if (!aligned(k_prev, 16) || !aligned(g_prev, 16) || !aligned(u_prev, 16) ||
+        !aligned(accepted_prev, 4))
+      return KDA_ERR_INVALID_ARG;
+    // u may reuse u_prev's buffer only row for row: with another draft
+    // length, one workgroup's new rows would be another's previous ones
+    if (u == u_prev && T != T_prev) return KDA_ERR_INVALID_ARG;
+  }
+  kda::SpecArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.state = state;
+  a.o = o;
+  a.u = u;
+  a.B = B; a.T = T; a.H = H;
+  a.dk = Dk; a.dv = Dv;
+  a.scale = scale;
+  a.T_prev = T_prev;
+  if (T_prev > 0) {
+    a.k_prev = k_prev; a.g_prev = g_prev; a.u_prev = u_prev;
+    a.accepted_prev = accepted_prev;
+  }
+  if (kda::launch_spec(a, tile_dim(Dk, Dv), dtype == KDA_DTYPE_BF16,
+                       kda::SpecMode::kStep,
                        static_cast<hipStream_t>(stream)) != hipSuccess)
     return KDA_ERR_LAUNCH;
   return KDA_OK;

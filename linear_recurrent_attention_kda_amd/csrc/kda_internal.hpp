@@ -119,7 +119,14 @@ struct SpecArgs {
   int32_t B, T, H;
   int32_t dk, dv;                                // head dims as stored
   float scale;
+  // previous draft, committed before the verify (step): its k, g and u
+  // [B, T_prev, H, D] and accepted counts [B]; T_prev = 0 when none
+  const void* k_prev; const float* g_prev; const float* u_prev;
+  const int32_t* accepted_prev;
+  int32_t T_prev;
 };
+
+enum class SpecMode { kVerify, kCommit, kStep };
 
 struct DecodeArgs {
   const void* q; const void* k; const void* v;
@@ -160,7 +167,7 @@ hipError_t launch_prep(const PrefillArgs& a, int D, int C, bool bf16_io,
                        hipStream_t s);
 hipError_t launch_recur(const PrefillArgs& a, int D, int C, bool bf16_io,
                         hipStream_t s);
-hipError_t launch_spec(const SpecArgs& a, int D, bool bf16_io, bool commit,
+hipError_t launch_spec(const SpecArgs& a, int D, bool bf16_io, SpecMode mode,
                        hipStream_t s);
 int max_spec_tokens();
 hipError_t launch_epilogue(const EpilogueArgs& a, int D, bool bf16_io,

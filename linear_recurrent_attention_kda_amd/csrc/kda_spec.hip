@@ -20,8 +20,13 @@
 //   [0, T]) the state is read once, the a updates S = Diag(exp g_t) S +
 //   k_t u_t^T are applied with the decode kernel's arithmetic, and the state
 //   is written once (not at all when a = 0).
+// step: commit of the previous draft's accepted prefix followed by verify
+//   of the new draft, in one pass: the state is read once, the accepted
+//   updates are applied and the state is written (when any was accepted),
+//   and the new draft is run from the registers.
 // State traffic per head: verify reads 4 d^2 bytes and commit reads and
-// writes 8 d^2, against 8 d^2 per accepted token for single decode steps.
+// writes 8 d^2, against 8 d^2 per accepted token for single decode steps; a
+// step reads and writes 8 d^2 where commit then verify move 12 d^2.
 #include <stdlib.h>
 
 #include "kda_device.hpp"
@@ -45,8 +50,23 @@ struct SpecTiling {
                 "spec tiling");
 };
 
-template <typename Tio, int D, int NT>
+// The commit's update of one state row group by token t: per element the
+// rounded product s <- alpha s, then one fused multiply-add s <- k u + s.
+// Both roundings are spelled out (no contraction left to the compiler), so
+// the commit and step kernels round alike whatever their unrolling.
+__device__ __forceinline__ void commit_update(float4& s, float al, float kc,
+                                              const float4& u) {
+#pragma clang fp contract(off)
+  s.x = s.x * al; s.y = s.y * al; s.z = s.z * al; s.w = s.w * al;
+  s.x = __builtin_fmaf(kc, u.x, s.x); s.y = __builtin_fmaf(kc, u.y, s.y);
+  s.z = __builtin_fmaf(kc, u.z, s.z); s.w = __builtin_fmaf(kc, u.w, s.w);
+}
+
+template <typename Tio, int D, int NT, bool kStep>
 __global__ __launch_bounds__(NT) void spec_verify_kernel(SpecArgs a) {
+  // every fused multiply-add below is written out: the verify and step
+  // instantiations then round alike
+#pragma clang fp contract(off)
   using Ti = SpecTiling<D, NT>;
   constexpr int CG = Ti::CG, RG = Ti::RG, RPT = Ti::RPT, NW = Ti::NW;
   __shared__ float s_alpha[kMaxSpecT][D], s_k[kMaxSpecT][D], s_q[kMaxSpecT][D];
@@ -64,14 +84,57 @@ __global__ __launch_bounds__(NT) void spec_verify_kernel(SpecArgs a) {
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(a.state + (size_t)bh * dk * dv, dk * dv * 4);
 
+  // a step touches the state once (read, then write): non-temporal
+  constexpr int kPolicy = kStep ? kCachePolicyNt : 0;
+  auto soff = [&](int c) {
+    return (c < dk && col_ok) ? (uint32_t)((c * dv + 4 * cg) * 4) : kOffNone;
+  };
   float4 s[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int c = rg + RG * i;
+  for (int i = 0; i < RPT; ++i)
     s[i] = __builtin_bit_cast(
-        float4, __builtin_amdgcn_raw_buffer_load_b128(
-                    rs, (c < dk && col_ok) ? (uint32_t)((c * dv + 4 * cg) * 4)
-                                           : kOffNone, 0, 0));
+        float4, __builtin_amdgcn_raw_buffer_load_b128(rs, soff(rg + RG * i),
+                                                      0, kPolicy));
+
+  if constexpr (kStep) {
+    // commit of the previous draft's first `acc` tokens (uniform per
+    // workgroup), exactly as spec_commit_kernel applies them
+    int acc = a.T_prev > 0 ? a.accepted_prev[b] : 0;
+    acc = acc < 0 ? 0 : (acc > a.T_prev ? a.T_prev : acc);
+    if (acc > 0) {
+      for (int e = tid; e < acc * D; e += NT) {
+        const int t = e / D, c = e % D;
+        const size_t row = ((size_t)b * a.T_prev + t) * a.H + h;
+        const bool ok = c < dk;
+        s_alpha[t][c] =
+            ok ? __builtin_amdgcn_exp2f(a.g_prev[row * dk + c] * kLog2e)
+               : 1.f;
+        s_k[t][c] = ok ? io<Tio>::to_f(
+                             static_cast<const Tio*>(a.k_prev)[row * dk + c])
+                       : 0.f;
+      }
+      __syncthreads();
+      for (int t = 0; t < acc; ++t) {
+        const size_t row = ((size_t)b * a.T_prev + t) * a.H + h;
+        const float4 u =
+            col_ok ? *reinterpret_cast<const float4*>(a.u_prev + row * dv +
+                                                      4 * cg)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          const int c = rg + RG * i;
+          commit_update(s[i], s_alpha[t][c], s_k[t][c], u);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < RPT; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4, s[i]), rs, soff(rg + RG * i), 0,
+            kCachePolicyNt);
+      // the staging arrays are refilled below, and u (which may be u_prev)
+      // is written only after every thread's reads of u_prev
+      __syncthreads();
+    }
   }
 
   // token t of sequence b, head h: row (b * T + t) * H + h
@@ -95,10 +158,17 @@ __global__ __launch_bounds__(NT) void spec_verify_kernel(SpecArgs a) {
     for (int i = 0; i < RPT; ++i) {
       const int c = rg + RG * i;
       const float al = s_alpha[t][c], kc = s_k[t][c], qc = s_q[t][c];
-      s[i].x *= al; s[i].y *= al; s[i].z *= al; s[i].w *= al;
-      x[0] += s[i].x * kc; x[1] += s[i].y * kc; x[2] += s[i].z * kc; x[3] += s[i].w * kc;
-      y[0] += s[i].x * qc; y[1] += s[i].y * qc; y[2] += s[i].z * qc; y[3] += s[i].w * qc;
-      qk += qc * kc;
+      s[i].x = s[i].x * al; s[i].y = s[i].y * al;
+      s[i].z = s[i].z * al; s[i].w = s[i].w * al;
+      x[0] = __builtin_fmaf(s[i].x, kc, x[0]);
+      x[1] = __builtin_fmaf(s[i].y, kc, x[1]);
+      x[2] = __builtin_fmaf(s[i].z, kc, x[2]);
+      x[3] = __builtin_fmaf(s[i].w, kc, x[3]);
+      y[0] = __builtin_fmaf(s[i].x, qc, y[0]);
+      y[1] = __builtin_fmaf(s[i].y, qc, y[1]);
+      y[2] = __builtin_fmaf(s[i].z, qc, y[2]);
+      y[3] = __builtin_fmaf(s[i].w, qc, y[3]);
+      qk = __builtin_fmaf(qc, kc, qk);
     }
 #pragma unroll
     for (int off = 32; off >= CG; off >>= 1) {
@@ -143,17 +213,19 @@ __global__ __launch_bounds__(NT) void spec_verify_kernel(SpecArgs a) {
     u.w = beta * (vv[3] - X.w);
     if (rg == 0 && col_ok) {
       Tio* o = static_cast<Tio*>(a.o) + row * dv + 4 * cg;
-      o[0] = io<Tio>::from_f(a.scale * (Y.x + QK * u.x));
-      o[1] = io<Tio>::from_f(a.scale * (Y.y + QK * u.y));
-      o[2] = io<Tio>::from_f(a.scale * (Y.z + QK * u.z));
-      o[3] = io<Tio>::from_f(a.scale * (Y.w + QK * u.w));
+      o[0] = io<Tio>::from_f(a.scale * __builtin_fmaf(QK, u.x, Y.x));
+      o[1] = io<Tio>::from_f(a.scale * __builtin_fmaf(QK, u.y, Y.y));
+      o[2] = io<Tio>::from_f(a.scale * __builtin_fmaf(QK, u.z, Y.z));
+      o[3] = io<Tio>::from_f(a.scale * __builtin_fmaf(QK, u.w, Y.w));
       *reinterpret_cast<float4*>(a.u + row * dv + 4 * cg) = u;
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const float kc = s_k[t][rg + RG * i];
-      s[i].x = s[i].x + kc * u.x; s[i].y = s[i].y + kc * u.y;
-      s[i].z = s[i].z + kc * u.z; s[i].w = s[i].w + kc * u.w;
+      s[i].x = __builtin_fmaf(kc, u.x, s[i].x);
+      s[i].y = __builtin_fmaf(kc, u.y, s[i].y);
+      s[i].z = __builtin_fmaf(kc, u.z, s[i].z);
+      s[i].w = __builtin_fmaf(kc, u.w, s[i].w);
     }
   }
 }
@@ -204,10 +276,7 @@ __global__ __launch_bounds__(NT) void spec_commit_kernel(SpecArgs a) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int c = rg + RG * i;
-      const float al = s_alpha[t][c], kc = s_k[t][c];
-      s[i].x *= al; s[i].y *= al; s[i].z *= al; s[i].w *= al;
-      s[i].x = s[i].x + kc * u.x; s[i].y = s[i].y + kc * u.y;
-      s[i].z = s[i].z + kc * u.z; s[i].w = s[i].w + kc * u.w;
+      commit_update(s[i], s_alpha[t][c], s_k[t][c], u);
     }
   }
 #pragma unroll
@@ -228,25 +297,28 @@ constexpr int spec_threads() {
 }
 
 template <typename Tio, int D>
-hipError_t launch_d(const SpecArgs& a, bool commit, hipStream_t st) {
+hipError_t launch_d(const SpecArgs& a, SpecMode mode, hipStream_t st) {
   const unsigned blocks = (unsigned)a.B * (unsigned)a.H;
-  if (commit) {
+  if (mode == SpecMode::kCommit) {
     constexpr int NT = spec_threads<D, 1024>();
     return launch_kernel(spec_commit_kernel<Tio, D, NT>, dim3(blocks),
                          dim3(NT), st, a);
   }
   constexpr int NT = spec_threads<D, 256>();
-  return launch_kernel(spec_verify_kernel<Tio, D, NT>, dim3(blocks), dim3(NT),
-                       st, a);
+  if (mode == SpecMode::kStep)
+    return launch_kernel(spec_verify_kernel<Tio, D, NT, true>, dim3(blocks),
+                         dim3(NT), st, a);
+  return launch_kernel(spec_verify_kernel<Tio, D, NT, false>, dim3(blocks),
+                       dim3(NT), st, a);
 }
 
 template <typename Tio>
-hipError_t launch_t(const SpecArgs& a, int D, bool commit, hipStream_t st) {
+hipError_t launch_t(const SpecArgs& a, int D, SpecMode mode, hipStream_t st) {
   switch (D) {
-    case 16: return launch_d<Tio, 16>(a, commit, st);
-    case 32: return launch_d<Tio, 32>(a, commit, st);
-    case 64: return launch_d<Tio, 64>(a, commit, st);
-    case 128: return launch_d<Tio, 128>(a, commit, st);
+    case 16: return launch_d<Tio, 16>(a, mode, st);
+    case 32: return launch_d<Tio, 32>(a, mode, st);
+    case 64: return launch_d<Tio, 64>(a, mode, st);
+    case 128: return launch_d<Tio, 128>(a, mode, st);
   }
   return hipErrorInvalidValue;
 }
@@ -255,10 +327,10 @@ hipError_t launch_t(const SpecArgs& a, int D, bool commit, hipStream_t st) {
 
 int max_spec_tokens() { return kMaxSpecT; }
 
-hipError_t launch_spec(const SpecArgs& a, int D, bool bf16_io, bool commit,
+hipError_t launch_spec(const SpecArgs& a, int D, bool bf16_io, SpecMode mode,
                        hipStream_t st) {
-  return bf16_io ? launch_t<bf16>(a, D, commit, st)
-                 : launch_t<float>(a, D, commit, st);
+  return bf16_io ? launch_t<bf16>(a, D, mode, st)
+                 : launch_t<float>(a, D, mode, st);
 }
 
 }  // namespace kda

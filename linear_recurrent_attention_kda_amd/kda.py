@@ -96,6 +96,10 @@ def load() -> ctypes.CDLL:
         lib.kda_spec_commit.restype = i32
         lib.kda_spec_commit.argtypes = [
             vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+        lib.kda_spec_step.restype = i32
+        lib.kda_spec_step.argtypes = [
+            vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+            i32, i32, i32, f32, i32, vp]
         lib.kda_output_norm_gate.restype = i32
         lib.kda_output_norm_gate.argtypes = [vp, vp, vp, f32, vp, i64, i32,
                                              i32, i32, vp]
@@ -611,6 +615,54 @@ def kda_spec_commit(k, g, u, accepted, state):
     if st != KDA_OK:
         raise KDAError("kda_spec_commit", st)
     return state
+
+
+def kda_spec_step(q, k, v, g, beta, state, *, k_prev=None, g_prev=None,
+                  u_prev=None, accepted_prev=None, scale: float = 1.0,
+                  o=None, u=None):
+    """Commit the previous draft's accepted prefix to `state` (in place) and
+    verify the new draft from the updated state, in one pass over the state:
+    kda_spec_commit(k_prev, g_prev, u_prev, accepted_prev, state) followed by
+    kda_spec_verify(q, k, v, g, beta, state), bit for bit.  Without k_prev
+    (no previous draft) it is kda_spec_verify.  u may be u_prev itself when
+    both drafts have the same length.  Returns (o, u)."""
+    lib = load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    for t, n, s_, dt in ((q, "q", (B, T, H, Dk), q.dtype),
+                         (k, "k", (B, T, H, Dk), q.dtype),
+                         (v, "v", (B, T, H, Dv), q.dtype),
+                         (g, "g", (B, T, H, Dk), torch.float32),
+                         (beta, "beta", (B, T, H), torch.float32),
+                         (state, "state", (B, H, Dk, Dv), torch.float32)):
+        _check(t, n, s_, dt, dev)
+    T_prev = 0
+    if k_prev is not None:
+        T_prev = k_prev.shape[1]
+        for t, n, s_, dt in ((k_prev, "k_prev", (B, T_prev, H, Dk), q.dtype),
+                             (g_prev, "g_prev", (B, T_prev, H, Dk),
+                              torch.float32),
+                             (u_prev, "u_prev", (B, T_prev, H, Dv),
+                              torch.float32),
+                             (accepted_prev, "accepted_prev", (B,),
+                              torch.int32)):
+            if t is None:
+                raise ValueError("%s is required with k_prev" % n)
+            _check(t, n, s_, dt, dev)
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev)
+    _check(o, "o", (B, T, H, Dv), q.dtype, dev)
+    if u is None:
+        u = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+    _check(u, "u", (B, T, H, Dv), torch.float32, dev)
+    st = lib.kda_spec_step(
+        _ptr(k_prev), _ptr(g_prev), _ptr(u_prev), _ptr(accepted_prev), T_prev,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+        _ptr(u), B, T, H, Dk, Dv, scale, _dtype_code(q), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_spec_step", st)
+    return o, u
 
 
 def kda_output_norm_gate(o, z, w, *, eps: float = 1e-6, y=None):

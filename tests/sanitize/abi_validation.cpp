@@ -65,6 +65,8 @@ int main() {
   expect("epilogue tokens=0", kda_output_norm_gate(P, P, F, 1e-6f, P, 0, 2, 128, 0, nullptr), KDA_OK);
   expect("verify T=17", kda_spec_verify(P, P, P, F, F, F, P, F, 2, 17, 2, 128, 128, 1.f, 0, nullptr), KDA_ERR_UNSUPPORTED);
   expect("commit acc NULL", kda_spec_commit(P, F, F, nullptr, F, 2, 4, 2, 128, 128, 0, nullptr), KDA_ERR_INVALID_ARG);
+  expect("step k_prev NULL", kda_spec_step(nullptr, F, F, I, 4, P, P, P, F, F, F, P, F, 2, 4, 2, 128, 128, 1.f, 0, nullptr), KDA_ERR_INVALID_ARG);
+  expect("step T_prev=17", kda_spec_step(P, F, F, I, 17, P, P, P, F, F, F, P, F, 2, 4, 2, 128, 128, 1.f, 0, nullptr), KDA_ERR_UNSUPPORTED);
 
   if (failures) {
     fprintf(stderr, "%d unexpected statuses\n", failures);

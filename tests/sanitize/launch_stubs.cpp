@@ -20,7 +20,7 @@ hipError_t launch_prep(const PrefillArgs&, int, int, bool, hipStream_t) {
 hipError_t launch_recur(const PrefillArgs&, int, int, bool, hipStream_t) {
   return hipErrorInvalidValue;
 }
-hipError_t launch_spec(const SpecArgs&, int, bool, bool, hipStream_t) {
+hipError_t launch_spec(const SpecArgs&, int, bool, SpecMode, hipStream_t) {
   return hipErrorInvalidValue;
 }
 hipError_t launch_epilogue(const EpilogueArgs&, int, bool, hipStream_t) {

@@ -37,7 +37,8 @@ def test_exports_every_declared_symbol():
                           "kda_prefill_varlen_noalloc",
                           "kda_prefill_varlen_gated",
                           "kda_decode_step", "kda_spec_verify",
-                          "kda_spec_commit", "kda_output_norm_gate",
+                          "kda_spec_commit", "kda_spec_step",
+                          "kda_output_norm_gate",
                           "kda_decode_step_gated",
                           "kda_prefill_varlen_prologue",
                           "kda_prefill_varlen_prep",
@@ -335,6 +336,41 @@ def _commit(lib, **kw):
     return lib.kda_spec_commit(a["k"], a["g"], a["u"], a["acc"], a["state"],
                                a["B"], a["T"], a["H"], a["Dk"], a["Dv"],
                                a["dtype"], a["stream"])
+
+
+def _step(lib, **kw):
+    a = dict(kp=P, gp=P, up=ctypes.c_void_p(0x200000), accp=P, Tp=4, q=P,
+             k=P, v=P, g=P, beta=P, state=P, o=P, u=P, B=2, T=4, H=2,
+             Dk=128, Dv=128, scale=1.0, dtype=0, stream=NULL)
+    a.update(kw)
+    return lib.kda_spec_step(a["kp"], a["gp"], a["up"], a["accp"], a["Tp"],
+                             a["q"], a["k"], a["v"], a["g"], a["beta"],
+                             a["state"], a["o"], a["u"], a["B"], a["T"],
+                             a["H"], a["Dk"], a["Dv"], a["scale"],
+                             a["dtype"], a["stream"])
+
+
+def test_spec_step_validation():
+    """Every call here fails validation (nothing is launched): the verify
+    checks, the previous draft's pointers when T_prev > 0, and u reusing
+    u_prev's buffer with another draft length."""
+    lib = kda.load()
+    assert _step(lib, T=0) == INVALID
+    assert _step(lib, T=17) == UNSUP
+    assert _step(lib, Tp=17) == UNSUP
+    assert _step(lib, Tp=-1) == INVALID
+    assert _step(lib, Dk=100, Dv=100) == UNSUP
+    assert _step(lib, u=NULL) == INVALID
+    assert _step(lib, q=NULL) == INVALID
+    for name in ("kp", "gp", "up", "accp"):
+        assert _step(lib, **{name: NULL}) == INVALID, name
+    assert _step(lib, accp=ctypes.c_void_p(0x100002)) == INVALID
+    assert _step(lib, up=MIS) == INVALID
+    assert _step(lib, up=P, T=3) == INVALID        # u == u_prev, T != T_prev
+    # with no previous draft its pointers are not looked at; the call would
+    # then launch, so only a failing verify check is exercised here
+    assert _step(lib, Tp=0, kp=NULL, gp=NULL, up=NULL, accp=NULL,
+                 T=17) == UNSUP
 
 
 def test_spec_validation():

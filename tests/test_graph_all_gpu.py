@@ -5,8 +5,9 @@ synchronising call), so a caller can capture them.  One graph holds: the
 varlen prefill, its two stages as separate calls, checkpoints at an interval
 and at listed positions, the gated prefill on both of its paths (fused into
 the recurrence, and plain prefill then the epilogue), the prologue-fused
-prefill, the standalone epilogue, the gated decode step, speculative verify
-and commit, and the prefill that uses the library's own scratch array.
+prefill, the standalone epilogue, the gated decode step, speculative verify,
+commit and the fused step, and the prefill that uses the library's own
+scratch array.
 Each replay, with eager resets and synchronisations between replays, must
 give the eager calls' results bit for bit."""
 import numpy as np
@@ -108,6 +109,10 @@ def test_graph_of_every_entry_point():
     so = torch.empty_like(sv)
     su = torch.empty(sv.shape, dtype=torch.float32, device=U.DEV)
     accepted = torch.tensor([0, 3, 6, 2], dtype=torch.int32, device=U.DEV)
+    # the fused step commits that draft to its own copy of the states and
+    # verifies the same tokens again
+    sstate2 = sstate0.clone()
+    so2, su2 = torch.empty_like(so), torch.empty_like(su)
 
     def varlen_args(x):
         return (x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu"],
@@ -154,18 +159,23 @@ def test_graph_of_every_entry_point():
                                   y=y_dec)
         kda.kda_spec_verify(sq, sk, sv, sg, sbeta, sstate, o=so, u=su)
         kda.kda_spec_commit(sk, sg, su, accepted, sstate)
+        kda.kda_spec_step(sq, sk, sv, sg, sbeta, sstate2, k_prev=sk,
+                          g_prev=sg, u_prev=su, accepted_prev=accepted,
+                          o=so2, u=su2)
         b = bufs["noalloc"]
         kda.kda_prefill_varlen_noalloc(*varlen_args(a), chunk_size=C,
                                        o=b["o"], final_state=b["fs"])
 
     results = [b[key] for b in bufs.values() for key in ("o", "fs", "ck")
-               if key in b] + [y_epi, y_dec, dstate, so, su, sstate]
+               if key in b] + [y_epi, y_dec, dstate, so, su, sstate, so2,
+                               su2, sstate2]
 
     def reset():
         for t in results:
             t.zero_()
         dstate.copy_(dstate0)        # updated in place by each step
         sstate.copy_(sstate0)
+        sstate2.copy_(sstate0)
 
     reset()
     step()
@@ -174,6 +184,8 @@ def test_graph_of_every_entry_point():
     # the stages equal the fused call; the eager step is deterministic
     assert torch.equal(bufs["stages"]["o"], bufs["varlen"]["o"])
     assert torch.equal(bufs["noalloc"]["o"], bufs["varlen"]["o"])
+    # the step's commit equals the separate commit
+    assert torch.equal(sstate2, sstate)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

@@ -1,0 +1,180 @@
+"""GPU tests of kda_spec_step: the commit of the previous draft's accepted
+prefix and the verify of the next draft in one pass over the state.
+
+Its contract is kda_spec_commit followed by kda_spec_verify, bit for bit
+(the same per-element arithmetic in the same order), so most cases compare
+the two paths exactly; both of them are checked against the fp64 oracle in
+test_spec_gpu.  A chain of steps is also checked against the oracle
+directly: the committed state after every step is the recurrence's state
+after all tokens accepted so far, and each draft's outputs are the
+recurrence's outputs over that draft from the committed state."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import gpu_available
+from linear_recurrent_attention_kda_amd import inputs, kda
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+import gpu_util as U  # noqa: E402
+
+
+def draft(seed, B, T, H, Dk, Dv, dtype):
+    """A draft of T tokens for each of B sequences, on the device, in the
+    [B, T, H, *] layout (plus the host problem)."""
+    p = inputs.make("varlen", seed=seed, H=H, K=Dk, V=Dv, dtype=dtype,
+                    lengths=[T] * B)
+    shp = lambda x: x.reshape((B, T) + x.shape[1:])  # noqa: E731
+    q, k, v = (U.to_dev(shp(x), p.dtype) for x in (p.q, p.k, p.v))
+    return p, (q, k, v, U.f32_dev(shp(p.g)), U.f32_dev(shp(p.beta)))
+
+
+CASES = [  # Dk, Dv, dtype, B, H, T_prev, T
+    (128, 128, "bf16", 5, 3, 4, 4),
+    (128, 128, "fp32", 3, 2, 8, 3),
+    (64, 128, "bf16", 4, 3, 2, 16),
+    (32, 32, "fp32", 6, 5, 16, 1),
+    (16, 48, "bf16", 3, 7, 5, 5),
+    (96, 64, "bf16", 2, 33, 1, 6),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_step_equals_commit_then_verify(case):
+    Dk, Dv, dtype, B, H, Tp, T = case
+    rng = np.random.default_rng(Dk + 3 * Dv + T)
+    # accepted counts: none, all, past the end (clamped), random
+    acc = [0, Tp, Tp + 3] + [int(x) for x in rng.integers(0, Tp + 1, B)]
+    acc = acc[:B]
+    U.log("spec step Dk=%d Dv=%d %s B=%d H=%d T_prev=%d T=%d accepted=%s"
+          % (Dk, Dv, dtype, B, H, Tp, T, acc))
+    p0, prev = draft(500 + T, B, Tp, H, Dk, Dv, dtype)
+    _, new = draft(600 + T, B, T, H, Dk, Dv, dtype)
+    s0 = U.f32_dev(p0.initial_state)
+    accepted = torch.tensor(acc, dtype=torch.int32, device=U.DEV)
+    # the previous draft's pseudo-values, from its own verify
+    _, u_prev = kda.kda_spec_verify(*prev, s0)
+    # two calls
+    st_a = s0.clone()
+    kda.kda_spec_commit(prev[1], prev[3], u_prev, accepted, st_a)
+    o_a, u_a = kda.kda_spec_verify(*new, st_a)
+    # one step
+    st_b = s0.clone()
+    o_b, u_b = kda.kda_spec_step(*new, st_b, k_prev=prev[1], g_prev=prev[3],
+                                 u_prev=u_prev, accepted_prev=accepted)
+    torch.cuda.synchronize()
+    assert torch.equal(st_a, st_b), "committed state"
+    assert torch.equal(o_a, o_b), "draft outputs"
+    assert torch.equal(u_a, u_b), "pseudo-values"
+    # sequences with nothing accepted keep their state bit for bit
+    for b, a in enumerate(acc):
+        if a == 0:
+            assert torch.equal(st_b[b], s0[b])
+    U.log("   state, outputs and pseudo-values equal commit + verify")
+
+
+def test_step_without_previous_draft_is_verify():
+    p, new = draft(701, 4, 6, 5, 128, 128, "bf16")
+    s0 = U.f32_dev(p.initial_state)
+    st = s0.clone()
+    o_a, u_a = kda.kda_spec_verify(*new, s0)
+    o_b, u_b = kda.kda_spec_step(*new, st)
+    torch.cuda.synchronize()
+    assert torch.equal(st, s0), "no previous draft: the state is unchanged"
+    assert torch.equal(o_a, o_b) and torch.equal(u_a, u_b)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_step_u_in_place(dtype):
+    """u written into the previous draft's u buffer (same draft length):
+    each workgroup reads its previous rows before writing its new ones."""
+    B, H, T, D = 6, 9, 5, 128
+    p0, prev = draft(710, B, T, H, D, D, dtype)
+    _, new = draft(711, B, T, H, D, D, dtype)
+    s0 = U.f32_dev(p0.initial_state)
+    accepted = torch.tensor([5, 0, 2, 7, 1, 3], dtype=torch.int32,
+                            device=U.DEV)
+    _, u_prev = kda.kda_spec_verify(*prev, s0)
+    st_a = s0.clone()
+    o_a, u_a = kda.kda_spec_step(*new, st_a, k_prev=prev[1], g_prev=prev[3],
+                                 u_prev=u_prev.clone(),
+                                 accepted_prev=accepted)
+    st_b = s0.clone()
+    u_buf = u_prev.clone()
+    o_b, u_b = kda.kda_spec_step(*new, st_b, k_prev=prev[1], g_prev=prev[3],
+                                 u_prev=u_buf, accepted_prev=accepted,
+                                 u=u_buf)
+    torch.cuda.synchronize()
+    assert u_b.data_ptr() == u_buf.data_ptr()
+    assert torch.equal(st_a, st_b) and torch.equal(o_a, o_b)
+    assert torch.equal(u_a, u_b)
+
+
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "fp32")])
+def test_step_chain_against_oracle(D, dtype):
+    """Four drafts in a row, each step committing the previous draft's
+    accepted prefix: the states and the drafts' outputs against the oracle
+    run over the accepted tokens."""
+    B, H, T = 4, 3, 6
+    rng = np.random.default_rng(720 + D)
+    p0, _ = draft(720, B, 1, H, D, D, dtype)
+    state = U.f32_dev(p0.initial_state)
+    s_ref = np.array(p0.initial_state, np.float64)
+    prev = None
+    for step in range(4):
+        p, new = draft(730 + step, B, T, H, D, D, dtype)
+        kw = {}
+        if prev is not None:
+            acc = [int(x) for x in rng.integers(0, T + 1, B)]
+            acc[step % B] = T
+            kw = dict(k_prev=prev[0][1], g_prev=prev[0][3], u_prev=prev[1],
+                      accepted_prev=torch.tensor(acc, dtype=torch.int32,
+                                                 device=U.DEV))
+            # the oracle commits the previous draft's accepted prefix
+            pp = prev[2]
+            for b, a in enumerate(acc):
+                if a:
+                    lo = b * T
+                    _, s = oracle.run_varlen(
+                        pp.q[lo:lo + a], pp.k[lo:lo + a], pp.v[lo:lo + a],
+                        pp.g[lo:lo + a], pp.beta[lo:lo + a],
+                        np.array([0, a]), s_ref[b:b + 1], want_output=False)
+                    s_ref[b] = s[0]
+        o, u = kda.kda_spec_step(*new, state, **kw)
+        torch.cuda.synchronize()
+        es = U.slice_rel(U.host(state), s_ref, (0, 1))
+        # this draft's outputs from the committed state
+        o_ref, _ = oracle.run_varlen(p.q, p.k, p.v, p.g, p.beta,
+                                     p.cu_seqlens, s_ref)
+        o_ref = o_ref.reshape((B, T) + o_ref.shape[1:])
+        oh = U.host(o)
+        eo = max(U.slice_rel(oh[b], o_ref[b], (1,)) for b in range(B))
+        U.log("   step %d: state rel err %.3e   draft o rel err %.3e"
+              % (step, es, eo))
+        assert es <= U.DECODE_STATE_TOL
+        assert eo <= U.DECODE_O_TOL[dtype]
+        prev = (new, u, p)
+
+
+def test_step_at_the_decode_workload():
+    """The decode batch (64 sequences x 96 heads, d = 128), T = 4 after a
+    4-token draft with mixed acceptance: equal to commit + verify."""
+    B, H, T = 64, 96, 4
+    p0, prev = draft(740, B, T, H, 128, 128, "bf16")
+    _, new = draft(741, B, T, H, 128, 128, "bf16")
+    s0 = U.f32_dev(p0.initial_state)
+    accepted = torch.tensor([b % (T + 1) for b in range(B)],
+                            dtype=torch.int32, device=U.DEV)
+    _, u_prev = kda.kda_spec_verify(*prev, s0)
+    st_a = s0.clone()
+    kda.kda_spec_commit(prev[1], prev[3], u_prev, accepted, st_a)
+    o_a, u_a = kda.kda_spec_verify(*new, st_a)
+    st_b = s0.clone()
+    o_b, u_b = kda.kda_spec_step(*new, st_b, k_prev=prev[1], g_prev=prev[3],
+                                 u_prev=u_prev, accepted_prev=accepted)
+    torch.cuda.synchronize()
+    assert torch.equal(st_a, st_b)
+    assert torch.equal(o_a, o_b) and torch.equal(u_a, u_b)
