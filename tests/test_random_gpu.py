@@ -168,6 +168,45 @@ def test_random_spec_verify_commit(seed):
 
 
 @pytest.mark.parametrize("seed", range(12))
+def test_random_spec_step(seed):
+    """kda_spec_step on random head dims, draft lengths (T_prev and T
+    apart) and acceptances, against kda_spec_commit then kda_spec_verify,
+    bit for bit."""
+    import torch
+    from linear_recurrent_attention_kda_amd import kda
+    rng = np.random.default_rng(700 + seed)
+    dims = [16 * i for i in range(1, 9)]
+    Dk, Dv = int(rng.choice(dims)), int(rng.choice(dims))
+    B, H = int(rng.integers(1, 9)), int(rng.choice([1, 2, 5, 33]))
+    Tp, T = int(rng.integers(1, 17)), int(rng.integers(1, 17))
+    dtype = "bf16" if rng.random() < 0.75 else "fp32"
+    acc = [int(a) for a in rng.integers(0, Tp + 2, size=B)]
+    U.log("random spec step %d: B=%d H=%d Dk=%d Dv=%d %s T_prev=%d T=%d "
+          "accepted=%s" % (seed, B, H, Dk, Dv, dtype, Tp, T, acc))
+
+    def draft(s, n):
+        p = inputs.make("varlen", seed=s, H=H, K=Dk, V=Dv, dtype=dtype,
+                        lengths=[n] * B)
+        shp = lambda x: x.reshape((B, n) + x.shape[1:])  # noqa: E731
+        q, k, v = (U.to_dev(shp(x), p.dtype) for x in (p.q, p.k, p.v))
+        return p, (q, k, v, U.f32_dev(shp(p.g)), U.f32_dev(shp(p.beta)))
+    p0, prev = draft(800 + seed, Tp)
+    _, new = draft(900 + seed, T)
+    s0 = U.f32_dev(p0.initial_state)
+    accepted = torch.tensor(acc, dtype=torch.int32, device=U.DEV)
+    _, u_prev = kda.kda_spec_verify(*prev, s0)
+    st_a = s0.clone()
+    kda.kda_spec_commit(prev[1], prev[3], u_prev, accepted, st_a)
+    o_a, u_a = kda.kda_spec_verify(*new, st_a)
+    st_b = s0.clone()
+    o_b, u_b = kda.kda_spec_step(*new, st_b, k_prev=prev[1], g_prev=prev[3],
+                                 u_prev=u_prev, accepted_prev=accepted)
+    torch.cuda.synchronize()
+    assert torch.equal(st_a, st_b) and torch.equal(o_a, o_b) and \
+        torch.equal(u_a, u_b)
+
+
+@pytest.mark.parametrize("seed", range(12))
 def test_random_prologue(seed):
     """kda_prefill_varlen_prologue (d_k = d_v) on random sizes and lengths.
     The kernel rounds the prologue's q, k and v to the storage dtype before
