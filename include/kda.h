@@ -93,8 +93,8 @@ const char* kda_status_string(int32_t status);
 
 /*
  * Bytes of device workspace that the prefill entry points (kda_prefill_chunked,
- * kda_prefill_varlen and its _ckpt, _ckpt_at, _gated, _prologue, _prep and
- * _recur forms; _noalloc holds it internally) need for N sequences holding
+ * kda_prefill_varlen and its _ckpt, _ckpt_at, _gated, _prologue, _indexed,
+ * _prep and _recur forms; _noalloc holds it internally) need for N sequences holding
  * total_T tokens (fixed length: N = B, total_T = B*T).  The workspace holds, per head and chunk, the chunk-prep
  * kernel's outputs that the chunk-recurrence kernel consumes ("FlashKDA
  * algorithm": K1 prepares chunk tensors in parallel, K2 runs the chunk-level
@@ -158,6 +158,31 @@ kda_status_t kda_prefill_varlen(const void* q, const void* k, const void* v,
                                 int32_t Dk, int32_t Dv, int32_t C, float scale,
                                 int32_t dtype, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * kda_prefill_varlen with the states kept in a pool ("Kimi K3: The Manos,
+ * The Mythos, The Legendos", section "Append-Prefill": a request continues
+ * from the recurrent state cached for it): sequence n starts from row
+ * state_idx[n] of state_pool and its final state is written back to the same
+ * row, so the caller need not gather and scatter states around the call.
+ *   state_pool  [pool_slots, H, Dk, Dv] fp32, read and updated in place.
+ *   state_idx   DEVICE int32 [N].  A slot outside [0, pool_slots) marks a
+ *               padding entry: it runs from a zero state and no state is read
+ *               or written for it.  Valid slots must be distinct.
+ *   has_initial DEVICE int32 [N] or NULL.  has_initial[n] == 0 starts
+ *               sequence n from zeros (a new request) instead of its row;
+ *               NULL means every sequence continues from its row.
+ * Results equal kda_prefill_varlen on the gathered states (zeros where
+ * has_initial is 0) followed by a scatter of its final states, bit for bit.
+ * pool_slots >= 1; other arguments and errors as kda_prefill_varlen.
+ */
+kda_status_t kda_prefill_varlen_indexed(
+    const void* q, const void* k, const void* v, const float* g,
+    const float* beta, const int32_t* cu_seqlens, int32_t N, int64_t total_T,
+    int32_t max_seqlen, float* state_pool, const int32_t* state_idx,
+    const int32_t* has_initial, int32_t pool_slots, void* o, int32_t H,
+    int32_t Dk, int32_t Dv, int32_t C, float scale, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kda_prefill_varlen with the block's output epilogue fused into the
@@ -356,6 +381,25 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v,
                              void* o, int32_t B, int32_t H, int32_t Dk,
                              int32_t Dv, float scale, int32_t dtype,
                              void* stream);
+
+/*
+ * kda_decode_step with the states kept in a pool (same sections): sequence
+ * b's state is row state_idx[b] of state_pool [pool_slots, H, Dk, Dv] fp32,
+ * read once and written once in place.  A slot outside [0, pool_slots)
+ * marks a padding entry (for example a batch padded to a fixed size): it
+ * runs from a zero state, its output is written, and no state is read or
+ * written for it.  Valid slots must be distinct.  state_idx is a DEVICE
+ * int32 array [B]; pool_slots >= 1.  Results equal kda_decode_step on the
+ * gathered states followed by a scatter, bit for bit.  Other arguments and
+ * errors as kda_decode_step.
+ */
+kda_status_t kda_decode_step_indexed(const void* q, const void* k,
+                                     const void* v, const float* g,
+                                     const float* beta, float* state_pool,
+                                     const int32_t* state_idx,
+                                     int32_t pool_slots, void* o, int32_t B,
+                                     int32_t H, int32_t Dk, int32_t Dv,
+                                     float scale, int32_t dtype, void* stream);
 
 /*
  * Output epilogue of the KDA block ("Kimi K3: The Manos, The Mythos, The

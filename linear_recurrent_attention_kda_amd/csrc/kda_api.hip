@@ -127,6 +127,13 @@ kda_status_t check_tensors(int64_t tokens, const void* q, const void* k,
 
 // State checkpoints requested by a prefill call: none, every `every` tokens
 // of each sequence, or at the listed positions (see kda.h).
+// A state pool for the prefill's initial and final states (both the pool).
+struct PoolOpts {
+  const int32_t* idx = nullptr;
+  const int32_t* has_initial = nullptr;
+  int32_t slots = 0;
+};
+
 struct CkptOpts {
   enum Mode { kNone, kEvery, kList } mode = kNone;
   int32_t every = 0;
@@ -186,7 +193,8 @@ kda_status_t prefill_varlen(const void* q, const void* k, const void* v,
                             bool validate_only = false,
                             const void* gate_z = nullptr,
                             const float* gate_w = nullptr,
-                            float gate_eps = 0.f) {
+                            float gate_eps = 0.f,
+                            const PoolOpts& pool = PoolOpts{}) {
   if (N <= 0 || total_T < 0 || max_seqlen < 0) return KDA_ERR_INVALID_ARG;
   if (total_T > 0 && max_seqlen == 0) return KDA_ERR_INVALID_ARG;
   kda_status_t st = check_prefill_common(H, Dk, Dv, C, dtype);
@@ -230,6 +238,9 @@ kda_status_t prefill_varlen(const void* q, const void* k, const void* v,
   a.gate_z = gate_z;
   a.gate_w = gate_w;
   a.gate_eps = gate_eps;
+  a.state_idx = pool.idx;
+  a.has_initial = pool.has_initial;
+  a.pool_slots = pool.slots;
   return run_prefill(a, C, dtype, workspace, workspace_bytes, stream, stages,
                      validate_only);
 }
@@ -238,7 +249,9 @@ kda_status_t decode_step(const void* q, const void* k, const void* v,
                          const float* g, const float* beta, float* state,
                          void* o, const void* z, const float* w, float eps,
                          int32_t B, int32_t H, int32_t Dk, int32_t Dv,
-                         float scale, int32_t dtype, void* stream) {
+                         float scale, int32_t dtype, void* stream,
+                         const int32_t* state_idx = nullptr,
+                         int32_t pool_slots = 0) {
   if (B <= 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERR_INVALID_ARG;
   if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_FP32)
     return KDA_ERR_UNSUPPORTED;
@@ -260,6 +273,8 @@ kda_status_t decode_step(const void* q, const void* k, const void* v,
   a.z = z;
   a.w = w;
   a.eps = eps;
+  a.state_idx = state_idx;
+  a.pool_slots = pool_slots;
   if (kda::launch_decode(a, tile_dim(Dk, Dv), dtype == KDA_DTYPE_BF16,
                          static_cast<hipStream_t>(stream)) != hipSuccess)
     return KDA_ERR_LAUNCH;
@@ -662,6 +677,42 @@ kda_status_t kda_spec_step(const void* k_prev, const float* g_prev,
                        static_cast<hipStream_t>(stream)) != hipSuccess)
     return KDA_ERR_LAUNCH;
   return KDA_OK;
+}
+
+kda_status_t kda_decode_step_indexed(const void* q, const void* k,
+                                     const void* v, const float* g,
+                                     const float* beta, float* state_pool,
+                                     const int32_t* state_idx,
+                                     int32_t pool_slots, void* o, int32_t B,
+                                     int32_t H, int32_t Dk, int32_t Dv,
+                                     float scale, int32_t dtype,
+                                     void* stream) {
+  if (pool_slots <= 0 || !state_idx || !aligned(state_idx, 4))
+    return KDA_ERR_INVALID_ARG;
+  return decode_step(q, k, v, g, beta, state_pool, o, nullptr, nullptr, 0.f,
+                     B, H, Dk, Dv, scale, dtype, stream, state_idx,
+                     pool_slots);
+}
+
+kda_status_t kda_prefill_varlen_indexed(
+    const void* q, const void* k, const void* v, const float* g,
+    const float* beta, const int32_t* cu_seqlens, int32_t N, int64_t total_T,
+    int32_t max_seqlen, float* state_pool, const int32_t* state_idx,
+    const int32_t* has_initial, int32_t pool_slots, void* o, int32_t H,
+    int32_t Dk, int32_t Dv, int32_t C, float scale, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  if (pool_slots <= 0 || !state_pool || !state_idx || !aligned(state_idx, 4) ||
+      (has_initial && !aligned(has_initial, 4)))
+    return KDA_ERR_INVALID_ARG;
+  PoolOpts pool;
+  pool.idx = state_idx;
+  pool.has_initial = has_initial;
+  pool.slots = pool_slots;
+  return prefill_varlen(q, k, v, g, beta, cu_seqlens, N, total_T, max_seqlen,
+                        state_pool, state_pool, o, H, Dk, Dv, C, scale, dtype,
+                        CkptOpts{}, nullptr, workspace, workspace_bytes,
+                        stream, kStagesBoth, false, nullptr, nullptr, 0.f,
+                        pool);
 }
 
 }  // extern "C"

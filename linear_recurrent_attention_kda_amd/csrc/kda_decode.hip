@@ -55,8 +55,19 @@ void decode_kernel(DecodeArgs a) {
   // compile time (constant strides, no masks)
   const int dk = kExact ? D : a.dk, dv = kExact ? D : a.dv;
   const bool col_ok = 4 * cg < dv;
-  float* S = a.state + (size_t)bh * dk * dv;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, dk * dv * 4);
+  // the state slice: row bh of [B, H, dk, dv], or, with a state pool, row
+  // (state_idx[b], h) of [pool_slots, H, dk, dv].  A padding entry (slot out
+  // of range) gets an empty buffer: its state loads read 0 and its stores
+  // are dropped, so it runs from a zero state and touches no state.
+  size_t srow = bh;
+  bool s_ok = true;
+  if (a.state_idx) {
+    const int32_t r = a.state_idx[bh / a.H];
+    s_ok = r >= 0 && r < a.pool_slots;
+    srow = s_ok ? (size_t)r * a.H + bh % a.H : 0;
+  }
+  float* S = a.state + srow * dk * dv;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, s_ok ? dk * dv * 4 : 0);
   constexpr int kPol = kNt ? kCachePolicyNt : 0;
   auto soff = [&](int c) {
     return (c < dk && col_ok) ? (uint32_t)((c * dv + 4 * cg) * 4) : kOffNone;

@@ -277,6 +277,33 @@ __device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int n,
   }
 }
 
+// Where sequence n's initial and final states live: row n of the
+// [N, H, dk, dv] arrays, or, with a state pool, row state_idx[n] of the
+// [pool_slots, H, dk, dv] pool.  A pool slot outside [0, pool_slots) marks
+// a padding entry: it starts from zero and no state is read or written for
+// it.  has_initial[n] == 0 starts sequence n from zero (its final state is
+// still written).  `base` is the element offset of head h's slice.
+struct StateSlot {
+  size_t base;
+  bool load, store;
+};
+__device__ __forceinline__ StateSlot state_slot(const PrefillArgs& a, int n,
+                                                int h, int dk, int dv) {
+  int64_t row = n;
+  bool ok = true, init = true;
+  if (a.state_idx) {
+    const int32_t r = a.state_idx[n];
+    ok = r >= 0 && r < a.pool_slots;
+    row = ok ? r : 0;
+    if (a.has_initial) init = a.has_initial[n] != 0;
+  }
+  StateSlot s;
+  s.base = ((size_t)row * a.H + h) * (size_t)dk * dv;
+  s.load = ok && init && a.initial_state != nullptr;
+  s.store = ok && a.final_state != nullptr;
+  return s;
+}
+
 // Chunks of sequence [bos, eos) that the recurrence walks: never more than
 // the chunk-prep grid covered (max_chunks, from the caller's max_seqlen), so
 // a max_seqlen below a sequence's length leaves that sequence's later tokens

@@ -107,6 +107,14 @@ struct PrefillArgs {
   const void* gate_z;
   const float* gate_w;
   float gate_eps;
+  // States kept in a pool (state_idx != nullptr): sequence n's initial and
+  // final states are row state_idx[n] of initial_state / final_state, both
+  // [pool_slots, H, dk, dv].  A slot outside [0, pool_slots) marks padding
+  // (zero start, no state read or written); has_initial[n] == 0, when
+  // has_initial is given, starts sequence n from zero.
+  const int32_t* state_idx;
+  const int32_t* has_initial;
+  int32_t pool_slots;
 };
 
 struct SpecArgs {
@@ -138,6 +146,11 @@ struct DecodeArgs {
   // output epilogue fused into the decode step (when z != nullptr): o is
   // replaced by o * rsqrt(mean(o^2) + eps) * w * sigmoid(z)
   const void* z; const float* w; float eps;
+  // state pool (state_idx != nullptr): sequence b's state is row
+  // state_idx[b] of `state` [pool_slots, H, dk, dv]; a slot outside
+  // [0, pool_slots) is padding (zero start, nothing read or written)
+  const int32_t* state_idx;
+  int32_t pool_slots;
 };
 
 struct EpilogueArgs {

@@ -120,7 +120,8 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
   // ---- initial state -> accumulators (D layout: row c = 16ct + 4kg + e,
   //      column j = 16jt + rl) and its bf16 copy -----------------------------
   f32x4 S[SPW];
-  const size_t sbase = ((size_t)n * H + h) * (size_t)dk * dv;
+  const StateSlot slot = state_slot(a, n, h, dk, dv);
+  const size_t sbase = slot.base;
   // element (row, col) of a stored dk x dv state slice, -1 when padded
   auto sidx = [&](int row, int col) -> int64_t {
     return (row < dk && col < dv) ? (int64_t)row * dv + col : -1;
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
     S[i] = zero4();
     if (t < NST) {
       const int ct = t / JT, jt = t % JT;
-      if (a.initial_state) {
+      if (slot.load) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int64_t ix = sidx(16 * ct + 4 * kg + e, j0 + 16 * jt + rl);
@@ -471,7 +472,7 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(PrefillArgs a) {
       if (ci + f < nchunks) process(ops[f], ci + f, ci + f + PF);
   }
 
-  if (a.final_state) {
+  if (slot.store) {
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const int t = s0t + i;
@@ -630,7 +631,8 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
   const int ct0 = s0t / JT;
 
   f32x4 S[SPW];
-  const size_t sbase = ((size_t)n * H + h) * (size_t)dk * dv;
+  const StateSlot slot = state_slot(a, n, h, dk, dv);
+  const size_t sbase = slot.base;
   // element (row, col) of a stored dk x dv state slice, -1 when padded
   auto sidx = [&](int row, int col) -> int64_t {
     return (row < dk && col < dv) ? (int64_t)row * dv + col : -1;
@@ -640,7 +642,7 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
     const int t = s0t + i;
     const int ct = t / JT, jt = t % JT;
     S[i] = zero4();
-    if (a.initial_state) {
+    if (slot.load) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t ix = sidx(16 * ct + 4 * kg + e, j0 + 16 * jt + rl);
@@ -783,7 +785,7 @@ __global__ __launch_bounds__(320, 1) void recur_stream_kernel(PrefillArgs a) {
     }
   }
 
-  if (a.final_state) {
+  if (slot.store) {
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const int t = s0t + i;

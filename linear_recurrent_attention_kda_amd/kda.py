@@ -114,6 +114,14 @@ def load() -> ctypes.CDLL:
         lib.kda_decode_step.restype = i32
         lib.kda_decode_step.argtypes = [
             vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
+        lib.kda_decode_step_indexed.restype = i32
+        lib.kda_decode_step_indexed.argtypes = [
+            vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, f32, i32,
+            vp]
+        lib.kda_prefill_varlen_indexed.restype = i32
+        lib.kda_prefill_varlen_indexed.argtypes = [
+            vp, vp, vp, vp, vp, vp, i32, i64, i32, vp, vp, vp, i32, vp, i32,
+            i32, i32, i32, f32, i32, vp, sz, vp]
         _lib = lib
         return lib
 
@@ -560,6 +568,79 @@ def kda_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, o=None):
                              _dtype_code(q), _stream(dev))
     if st != KDA_OK:
         raise KDAError("kda_decode_step", st)
+    return o
+
+
+def kda_decode_step_indexed(q, k, v, g, beta, state_pool, state_idx, *,
+                            scale: float = 1.0, o=None):
+    """kda_decode_step with the states in a pool: sequence b uses row
+    state_idx[b] (device int32 [B]) of state_pool [slots, H, Dk, Dv] fp32,
+    updated in place; a slot outside [0, slots) is padding (zero state,
+    nothing read or written).  Returns o [B, H, Dv]."""
+    lib = load()
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    slots = state_pool.shape[0]
+    for t, n, s, dt in ((q, "q", (B, H, Dk), q.dtype),
+                        (k, "k", (B, H, Dk), q.dtype),
+                        (v, "v", (B, H, Dv), q.dtype),
+                        (g, "g", (B, H, Dk), torch.float32),
+                        (beta, "beta", (B, H), torch.float32),
+                        (state_pool, "state_pool", (slots, H, Dk, Dv),
+                         torch.float32),
+                        (state_idx, "state_idx", (B,), torch.int32)):
+        _check(t, n, s, dt, dev)
+    if o is None:
+        o = torch.empty((B, H, Dv), dtype=q.dtype, device=dev)
+    _check(o, "o", (B, H, Dv), q.dtype, dev)
+    st = lib.kda_decode_step_indexed(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+        _ptr(state_idx), slots, _ptr(o), B, H, Dk, Dv, scale, _dtype_code(q),
+        _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_decode_step_indexed", st)
+    return o
+
+
+def kda_prefill_varlen_indexed(q, k, v, g, beta, cu_seqlens, max_seqlen: int,
+                               state_pool, state_idx, has_initial=None, *,
+                               chunk_size: int = 64, scale: float = 1.0,
+                               o=None, workspace=None):
+    """kda_prefill_varlen with the states in a pool: sequence n starts from
+    row state_idx[n] of state_pool [slots, H, Dk, Dv] fp32 (from zeros where
+    has_initial[n] == 0) and its final state is written back to that row.
+    A slot outside [0, slots) is padding.  Returns o."""
+    lib = load()
+    total_T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    N = cu_seqlens.numel() - 1
+    slots = state_pool.shape[0]
+    for t, n, s, dt in ((q, "q", (total_T, H, Dk), q.dtype),
+                        (k, "k", (total_T, H, Dk), q.dtype),
+                        (v, "v", (total_T, H, Dv), q.dtype),
+                        (g, "g", (total_T, H, Dk), torch.float32),
+                        (beta, "beta", (total_T, H), torch.float32),
+                        (cu_seqlens, "cu_seqlens", (N + 1,), torch.int32),
+                        (state_pool, "state_pool", (slots, H, Dk, Dv),
+                         torch.float32),
+                        (state_idx, "state_idx", (N,), torch.int32)):
+        _check(t, n, s, dt, dev)
+    if has_initial is not None:
+        _check(has_initial, "has_initial", (N,), torch.int32, dev)
+    if o is None:
+        o = torch.empty((total_T, H, Dv), dtype=q.dtype, device=dev)
+    _check(o, "o", (total_T, H, Dv), q.dtype, dev)
+    if workspace is None:
+        workspace = workspace_for(N, total_T, H, Dk, Dv, chunk_size, dev)
+    st = lib.kda_prefill_varlen_indexed(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N,
+        total_T, int(max_seqlen), _ptr(state_pool), _ptr(state_idx),
+        _ptr(has_initial), slots, _ptr(o), H, Dk, Dv, chunk_size, scale,
+        _dtype_code(q), _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_prefill_varlen_indexed", st)
     return o
 
 

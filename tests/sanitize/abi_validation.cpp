@@ -67,6 +67,8 @@ int main() {
   expect("commit acc NULL", kda_spec_commit(P, F, F, nullptr, F, 2, 4, 2, 128, 128, 0, nullptr), KDA_ERR_INVALID_ARG);
   expect("step k_prev NULL", kda_spec_step(nullptr, F, F, I, 4, P, P, P, F, F, F, P, F, 2, 4, 2, 128, 128, 1.f, 0, nullptr), KDA_ERR_INVALID_ARG);
   expect("step T_prev=17", kda_spec_step(P, F, F, I, 17, P, P, P, F, F, F, P, F, 2, 4, 2, 128, 128, 1.f, 0, nullptr), KDA_ERR_UNSUPPORTED);
+  expect("decode pool idx NULL", kda_decode_step_indexed(P, P, P, F, F, F, nullptr, 4, P, 2, 2, 128, 128, 1.f, 0, nullptr), KDA_ERR_INVALID_ARG);
+  expect("prefill pool slots 0", kda_prefill_varlen_indexed(P, P, P, F, F, I, 2, 100, 64, F, I, nullptr, 0, P, 2, 128, 128, 64, 1.f, 0, P, big, nullptr), KDA_ERR_INVALID_ARG);
 
   if (failures) {
     fprintf(stderr, "%d unexpected statuses\n", failures);

@@ -36,7 +36,8 @@ def test_exports_every_declared_symbol():
                           "kda_prefill_varlen_ckpt_at",
                           "kda_prefill_varlen_noalloc",
                           "kda_prefill_varlen_gated",
-                          "kda_decode_step", "kda_spec_verify",
+                          "kda_decode_step", "kda_decode_step_indexed",
+                          "kda_prefill_varlen_indexed", "kda_spec_verify",
                           "kda_spec_commit", "kda_spec_step",
                           "kda_output_norm_gate",
                           "kda_decode_step_gated",
@@ -371,6 +372,49 @@ def test_spec_step_validation():
     # then launch, so only a failing verify check is exercised here
     assert _step(lib, Tp=0, kp=NULL, gp=NULL, up=NULL, accp=NULL,
                  T=17) == UNSUP
+
+
+def _dec_idx(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, pool=P, idx=P, slots=4, o=P, B=2,
+             H=2, Dk=128, Dv=128, scale=1.0, dtype=0, stream=NULL)
+    a.update(kw)
+    return lib.kda_decode_step_indexed(
+        a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"], a["idx"],
+        a["slots"], a["o"], a["B"], a["H"], a["Dk"], a["Dv"], a["scale"],
+        a["dtype"], a["stream"])
+
+
+def _pre_idx(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, cu=P, N=2, T=100, maxlen=64,
+             pool=P, idx=P, hi=NULL, slots=4, o=P, H=2, Dk=128, Dv=128, C=64,
+             scale=1.0, dtype=0, ws=P, ws_bytes=1 << 40, stream=NULL)
+    a.update(kw)
+    return lib.kda_prefill_varlen_indexed(
+        a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"], a["T"],
+        a["maxlen"], a["pool"], a["idx"], a["hi"], a["slots"], a["o"],
+        a["H"], a["Dk"], a["Dv"], a["C"], a["scale"], a["dtype"], a["ws"],
+        a["ws_bytes"], a["stream"])
+
+
+def test_indexed_validation():
+    """The state-pool forms check the pool's own arguments first, then
+    everything the plain calls check (nothing is launched)."""
+    lib = kda.load()
+    assert _dec_idx(lib, slots=0) == INVALID
+    assert _dec_idx(lib, idx=NULL) == INVALID
+    assert _dec_idx(lib, idx=ctypes.c_void_p(0x100002)) == INVALID
+    assert _dec_idx(lib, pool=NULL) == INVALID
+    assert _dec_idx(lib, pool=MIS) == INVALID
+    assert _dec_idx(lib, B=0) == INVALID
+    assert _dec_idx(lib, Dk=40, Dv=40) == UNSUP
+    assert _pre_idx(lib, slots=-1) == INVALID
+    assert _pre_idx(lib, pool=NULL) == INVALID
+    assert _pre_idx(lib, idx=NULL) == INVALID
+    assert _pre_idx(lib, hi=ctypes.c_void_p(0x100002)) == INVALID
+    assert _pre_idx(lib, pool=MIS) == INVALID
+    assert _pre_idx(lib, N=0) == INVALID
+    assert _pre_idx(lib, C=8) == UNSUP
+    assert _pre_idx(lib, ws_bytes=10) == WS
 
 
 def test_spec_validation():

@@ -6,8 +6,8 @@ varlen prefill, its two stages as separate calls, checkpoints at an interval
 and at listed positions, the gated prefill on both of its paths (fused into
 the recurrence, and plain prefill then the epilogue), the prologue-fused
 prefill, the standalone epilogue, the gated decode step, speculative verify,
-commit and the fused step, and the prefill that uses the library's own
-scratch array.
+commit and the fused step, the prefill that uses the library's own
+scratch array, and the state-pool forms of prefill and decode.
 Each replay, with eager resets and synchronisations between replays, must
 give the eager calls' results bit for bit."""
 import numpy as np
@@ -113,6 +113,19 @@ def test_graph_of_every_entry_point():
     # verifies the same tokens again
     sstate2 = sstate0.clone()
     so2, su2 = torch.empty_like(so), torch.empty_like(su)
+    # state pools: the varlen sequences and the decode batch in pool rows
+    pv_pool0 = torch.randn((6, a["H"], a["K"], a["V"]), device=U.DEV) * 0.02
+    pv_pool = pv_pool0.clone()
+    pv_idx = torch.tensor([4, 0, -1, 2], dtype=torch.int32, device=U.DEV)
+    pv_has = torch.tensor([1, 0, 1, 1], dtype=torch.int32, device=U.DEV)
+    pv_o = out(a)
+    pv_ws = ws(a)
+    dpool0 = torch.randn((20,) + tuple(dstate0.shape[1:]),
+                         device=U.DEV) * 0.02
+    dpool = dpool0.clone()
+    didx = torch.tensor([(3 * b + 1) % 20 for b in range(pd.B)],
+                        dtype=torch.int32, device=U.DEV)
+    od_idx = torch.empty_like(dv)
 
     def varlen_args(x):
         return (x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu"],
@@ -165,10 +178,16 @@ def test_graph_of_every_entry_point():
         b = bufs["noalloc"]
         kda.kda_prefill_varlen_noalloc(*varlen_args(a), chunk_size=C,
                                        o=b["o"], final_state=b["fs"])
+        kda.kda_prefill_varlen_indexed(a["q"], a["k"], a["v"], a["g"],
+                                       a["beta"], a["cu"], a["maxlen"],
+                                       pv_pool, pv_idx, pv_has, chunk_size=C,
+                                       o=pv_o, workspace=pv_ws)
+        kda.kda_decode_step_indexed(dq, dk, dv, dg, dbeta, dpool, didx,
+                                    o=od_idx)
 
     results = [b[key] for b in bufs.values() for key in ("o", "fs", "ck")
                if key in b] + [y_epi, y_dec, dstate, so, su, sstate, so2,
-                               su2, sstate2]
+                               su2, sstate2, pv_o, pv_pool, dpool, od_idx]
 
     def reset():
         for t in results:
@@ -176,6 +195,8 @@ def test_graph_of_every_entry_point():
         dstate.copy_(dstate0)        # updated in place by each step
         sstate.copy_(sstate0)
         sstate2.copy_(sstate0)
+        pv_pool.copy_(pv_pool0)
+        dpool.copy_(dpool0)
 
     reset()
     step()
