@@ -436,6 +436,21 @@ kda_status_t kda_decode_step_gated(const void* q, const void* k,
                                    void* stream);
 
 /*
+ * kda_decode_step_gated on states kept in a pool, with the pool, index and
+ * padding rules of kda_decode_step_indexed (a padding entry runs from a zero
+ * state, its y is written, and no state is read or written for it).
+ * Results equal kda_decode_step_gated on the gathered states followed by a
+ * scatter, bit for bit.  Other arguments and errors as
+ * kda_decode_step_gated; pool_slots >= 1.
+ */
+kda_status_t kda_decode_step_gated_indexed(
+    const void* q, const void* k, const void* v, const float* g,
+    const float* beta, float* state_pool, const int32_t* state_idx,
+    int32_t pool_slots, const void* z, const float* w, float eps, void* y,
+    int32_t B, int32_t H, int32_t Dk, int32_t Dv, float scale, int32_t dtype,
+    void* stream);
+
+/*
  * Speculative-decode verify ("Model evolution after DeepSeek V3",
  * uncledou.site, section four: a cheap draft proposes several tokens and the
  * large model checks them in one parallel pass).  Runs T draft tokens of each
@@ -484,13 +499,15 @@ kda_status_t kda_spec_commit(const void* k, const float* g, const float* u,
  *   its verify (or step) wrote; accepted_prev: DEVICE int32 [B], clamped to
  *   [0, T_prev] (0: that sequence's state is neither changed nor written).
  *   T_prev = 0 means no previous draft: the four pointers are ignored (may
- *   be NULL) and the call is kda_spec_verify on `state`.
+ *   be NULL) and the call is kda_spec_verify on `state`.  T = 0 means no
+ *   new draft: q, k, v, g, beta, o and u are ignored and the call is
+ *   kda_spec_commit (with both 0 nothing is enqueued).
  *   state [B, H, Dk, Dv] fp32, updated in place by the commit only.
  *   u may be the very buffer u_prev when T == T_prev (each workgroup reads
  *   its previous rows before writing its new ones); any other overlap of u
  *   with u_prev, or with the inputs, is not allowed.  u == u_prev with
  *   T != T_prev returns KDA_ERR_INVALID_ARG.
- * Other arguments as kda_spec_verify; 0 <= T_prev <= 16.
+ * Other arguments as kda_spec_verify; 0 <= T, T_prev <= 16.
  */
 kda_status_t kda_spec_step(const void* k_prev, const float* g_prev,
                            const float* u_prev, const int32_t* accepted_prev,
@@ -499,6 +516,23 @@ kda_status_t kda_spec_step(const void* k_prev, const float* g_prev,
                            float* state, void* o, float* u, int32_t B,
                            int32_t T, int32_t H, int32_t Dk, int32_t Dv,
                            float scale, int32_t dtype, void* stream);
+
+/*
+ * kda_spec_step on states kept in a pool: sequence b's state is row
+ * state_idx[b] (DEVICE int32 [B]) of state_pool [pool_slots, H, Dk, Dv]
+ * fp32.  A slot outside [0, pool_slots) marks a padding entry: its draft
+ * runs from a zero state and no state is read or written for it.  Valid
+ * slots must be distinct.  Results equal kda_spec_step on the gathered
+ * states followed by a scatter, bit for bit.  pool_slots >= 1; other
+ * arguments and errors as kda_spec_step.
+ */
+kda_status_t kda_spec_step_indexed(
+    const void* k_prev, const float* g_prev, const float* u_prev,
+    const int32_t* accepted_prev, int32_t T_prev, const void* q,
+    const void* k, const void* v, const float* g, const float* beta,
+    float* state_pool, const int32_t* state_idx, int32_t pool_slots, void* o,
+    float* u, int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+    float scale, int32_t dtype, void* stream);
 
 #ifdef __cplusplus
 }

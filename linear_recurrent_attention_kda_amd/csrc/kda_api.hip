@@ -281,6 +281,64 @@ kda_status_t decode_step(const void* q, const void* k, const void* v,
   return KDA_OK;
 }
 
+// One speculative step (the commit of the previous draft, then the verify
+// of the next), on a state array or a state pool.  T == 0 commits only;
+// T_prev == 0 verifies only; with both 0 there is nothing to do.
+kda_status_t spec_step(const void* k_prev, const float* g_prev,
+                       const float* u_prev, const int32_t* accepted_prev,
+                       int32_t T_prev, const void* q, const void* k,
+                       const void* v, const float* g, const float* beta,
+                       float* state, void* o, float* u, int32_t B, int32_t T,
+                       int32_t H, int32_t Dk, int32_t Dv, float scale,
+                       int32_t dtype, void* stream,
+                       const int32_t* state_idx, int32_t pool_slots) {
+  if (B <= 0 || H <= 0 || T < 0 || Dk <= 0 || Dv <= 0 || T_prev < 0)
+    return KDA_ERR_INVALID_ARG;
+  if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_FP32)
+    return KDA_ERR_UNSUPPORTED;
+  if (!supported_dims(Dk, Dv) || T > kda::max_spec_tokens() ||
+      T_prev > kda::max_spec_tokens())
+    return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > INT_MAX) return KDA_ERR_UNSUPPORTED;
+  if (!state || !aligned(state, 16)) return KDA_ERR_INVALID_ARG;
+  if (T > 0) {
+    kda_status_t st = check_tensors((int64_t)B * T, q, k, v, g, beta, o);
+    if (st != KDA_OK) return st;
+    if (!u || !aligned(u, 16)) return KDA_ERR_INVALID_ARG;
+  }
+  if (T_prev > 0) {
+    if (!k_prev || !g_prev || !u_prev || !accepted_prev)
+      return KDA_ERR_INVALID_ARG;
+    if (!aligned(k_prev, 16) || !aligned(g_prev, 16) || !aligned(u_prev, 16) ||
+        !aligned(accepted_prev, 4))
+      return KDA_ERR_INVALID_ARG;
+    // u may reuse u_prev's buffer only row for row: with another draft
+    // length, one workgroup's new rows would be another's previous ones
+    if (T > 0 && u == u_prev && T != T_prev) return KDA_ERR_INVALID_ARG;
+  }
+  if (T == 0 && T_prev == 0) return KDA_OK;  // nothing to do
+  kda::SpecArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.state = state;
+  a.o = o;
+  a.u = u;
+  a.B = B; a.T = T; a.H = H;
+  a.dk = Dk; a.dv = Dv;
+  a.scale = scale;
+  a.T_prev = T_prev;
+  if (T_prev > 0) {
+    a.k_prev = k_prev; a.g_prev = g_prev; a.u_prev = u_prev;
+    a.accepted_prev = accepted_prev;
+  }
+  a.state_idx = state_idx;
+  a.pool_slots = pool_slots;
+  if (kda::launch_spec(a, tile_dim(Dk, Dv), dtype == KDA_DTYPE_BF16,
+                       kda::SpecMode::kStep,
+                       static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KDA_ERR_LAUNCH;
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -637,46 +695,37 @@ kda_status_t kda_spec_step(const void* k_prev, const float* g_prev,
                            float* state, void* o, float* u, int32_t B,
                            int32_t T, int32_t H, int32_t Dk, int32_t Dv,
                            float scale, int32_t dtype, void* stream) {
-  if (B <= 0 || H <= 0 || T <= 0 || Dk <= 0 || Dv <= 0 || T_prev < 0)
+  return spec_step(k_prev, g_prev, u_prev, accepted_prev, T_prev, q, k, v, g,
+                   beta, state, o, u, B, T, H, Dk, Dv, scale, dtype, stream,
+                   nullptr, 0);
+}
+
+kda_status_t kda_spec_step_indexed(
+    const void* k_prev, const float* g_prev, const float* u_prev,
+    const int32_t* accepted_prev, int32_t T_prev, const void* q,
+    const void* k, const void* v, const float* g, const float* beta,
+    float* state_pool, const int32_t* state_idx, int32_t pool_slots, void* o,
+    float* u, int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+    float scale, int32_t dtype, void* stream) {
+  if (pool_slots <= 0 || !state_idx || !aligned(state_idx, 4))
     return KDA_ERR_INVALID_ARG;
-  if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_FP32)
-    return KDA_ERR_UNSUPPORTED;
-  if (!supported_dims(Dk, Dv) || T > kda::max_spec_tokens() ||
-      T_prev > kda::max_spec_tokens())
-    return KDA_ERR_UNSUPPORTED;
-  if ((int64_t)B * H > INT_MAX) return KDA_ERR_UNSUPPORTED;
-  kda_status_t st = check_tensors((int64_t)B * T, q, k, v, g, beta, o);
-  if (st != KDA_OK) return st;
-  if (!state || !aligned(state, 16) || !u || !aligned(u, 16))
+  return spec_step(k_prev, g_prev, u_prev, accepted_prev, T_prev, q, k, v, g,
+                   beta, state_pool, o, u, B, T, H, Dk, Dv, scale, dtype,
+                   stream, state_idx, pool_slots);
+}
+
+kda_status_t kda_decode_step_gated_indexed(
+    const void* q, const void* k, const void* v, const float* g,
+    const float* beta, float* state_pool, const int32_t* state_idx,
+    int32_t pool_slots, const void* z, const float* w, float eps, void* y,
+    int32_t B, int32_t H, int32_t Dk, int32_t Dv, float scale, int32_t dtype,
+    void* stream) {
+  if (pool_slots <= 0 || !state_idx || !aligned(state_idx, 4))
     return KDA_ERR_INVALID_ARG;
-  if (T_prev > 0) {
-    if (!k_prev || !g_prev || !u_prev || !accepted_prev)
-      return KDA_ERR_INVALID_ARG;
-    if (!aligned(k_prev, 16) || !aligned(g_prev, 16) || !aligned(u_prev, 16) ||
-        !aligned(accepted_prev, 4))
-      return KDA_ERR_INVALID_ARG;
-    // u may reuse u_prev's buffer only row for row: with another draft
-    // length, one workgroup's new rows would be another's previous ones
-    if (u == u_prev && T != T_prev) return KDA_ERR_INVALID_ARG;
-  }
-  kda::SpecArgs a{};
-  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
-  a.state = state;
-  a.o = o;
-  a.u = u;
-  a.B = B; a.T = T; a.H = H;
-  a.dk = Dk; a.dv = Dv;
-  a.scale = scale;
-  a.T_prev = T_prev;
-  if (T_prev > 0) {
-    a.k_prev = k_prev; a.g_prev = g_prev; a.u_prev = u_prev;
-    a.accepted_prev = accepted_prev;
-  }
-  if (kda::launch_spec(a, tile_dim(Dk, Dv), dtype == KDA_DTYPE_BF16,
-                       kda::SpecMode::kStep,
-                       static_cast<hipStream_t>(stream)) != hipSuccess)
-    return KDA_ERR_LAUNCH;
-  return KDA_OK;
+  if (!z || !w || !aligned(z, 16) || !aligned(w, 16) || !(eps >= 0.f))
+    return KDA_ERR_INVALID_ARG;
+  return decode_step(q, k, v, g, beta, state_pool, y, z, w, eps, B, H, Dk, Dv,
+                     scale, dtype, stream, state_idx, pool_slots);
 }
 
 kda_status_t kda_decode_step_indexed(const void* q, const void* k,

@@ -132,6 +132,11 @@ struct SpecArgs {
   const void* k_prev; const float* g_prev; const float* u_prev;
   const int32_t* accepted_prev;
   int32_t T_prev;
+  // state pool (state_idx != nullptr): sequence b's state is row
+  // state_idx[b] of `state` [pool_slots, H, dk, dv]; a slot outside
+  // [0, pool_slots) is padding (zero state, nothing read or written)
+  const int32_t* state_idx;
+  int32_t pool_slots;
 };
 
 enum class SpecMode { kVerify, kCommit, kStep };

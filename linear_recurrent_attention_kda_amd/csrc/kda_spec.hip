@@ -62,6 +62,23 @@ __device__ __forceinline__ void commit_update(float4& s, float al, float kc,
   s.z = __builtin_fmaf(kc, u.z, s.z); s.w = __builtin_fmaf(kc, u.w, s.w);
 }
 
+// The state slice of (sequence, head) bh: row bh of [B, H, dk, dv], or,
+// with a state pool, row (state_idx[b], h) of [pool_slots, H, dk, dv].  A
+// padding entry (slot out of range) gets an empty buffer: its state loads
+// read 0 and its stores are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t spec_state(const SpecArgs& a,
+                                                            int bh, int dk,
+                                                            int dv) {
+  size_t row = bh;
+  bool ok = true;
+  if (a.state_idx) {
+    const int32_t r = a.state_idx[bh / a.H];
+    ok = r >= 0 && r < a.pool_slots;
+    row = ok ? (size_t)r * a.H + bh % a.H : 0;
+  }
+  return make_rsrc(a.state + row * dk * dv, ok ? dk * dv * 4 : 0);
+}
+
 template <typename Tio, int D, int NT, bool kStep>
 __global__ __launch_bounds__(NT) void spec_verify_kernel(SpecArgs a) {
   // every fused multiply-add below is written out: the verify and step
@@ -81,8 +98,7 @@ __global__ __launch_bounds__(NT) void spec_verify_kernel(SpecArgs a) {
   // are zero here and never stored
   const int dk = a.dk, dv = a.dv;
   const bool col_ok = 4 * cg < dv;
-  const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(a.state + (size_t)bh * dk * dv, dk * dv * 4);
+  const __amdgpu_buffer_rsrc_t rs = spec_state(a, bh, dk, dv);
 
   // a step touches the state once (read, then write): non-temporal
   constexpr int kPolicy = kStep ? kCachePolicyNt : 0;
@@ -247,8 +263,7 @@ __global__ __launch_bounds__(NT) void spec_commit_kernel(SpecArgs a) {
 
   const int dk = a.dk, dv = a.dv;
   const bool col_ok = 4 * cg < dv;
-  float* S = a.state + (size_t)bh * dk * dv;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, dk * dv * 4);
+  const __amdgpu_buffer_rsrc_t rs = spec_state(a, bh, dk, dv);
   auto soff = [&](int c) {
     return (c < dk && col_ok) ? (uint32_t)((c * dv + 4 * cg) * 4) : kOffNone;
   };

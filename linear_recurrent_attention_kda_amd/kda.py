@@ -100,6 +100,14 @@ def load() -> ctypes.CDLL:
         lib.kda_spec_step.argtypes = [
             vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
             i32, i32, i32, f32, i32, vp]
+        lib.kda_spec_step_indexed.restype = i32
+        lib.kda_spec_step_indexed.argtypes = [
+            vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32,
+            i32, i32, i32, i32, f32, i32, vp]
+        lib.kda_decode_step_gated_indexed.restype = i32
+        lib.kda_decode_step_gated_indexed.argtypes = [
+            vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, f32, vp, i32, i32, i32,
+            i32, f32, i32, vp]
         lib.kda_output_norm_gate.restype = i32
         lib.kda_output_norm_gate.argtypes = [vp, vp, vp, f32, vp, i64, i32,
                                              i32, i32, vp]
@@ -698,15 +706,8 @@ def kda_spec_commit(k, g, u, accepted, state):
     return state
 
 
-def kda_spec_step(q, k, v, g, beta, state, *, k_prev=None, g_prev=None,
-                  u_prev=None, accepted_prev=None, scale: float = 1.0,
-                  o=None, u=None):
-    """Commit the previous draft's accepted prefix to `state` (in place) and
-    verify the new draft from the updated state, in one pass over the state:
-    kda_spec_commit(k_prev, g_prev, u_prev, accepted_prev, state) followed by
-    kda_spec_verify(q, k, v, g, beta, state), bit for bit.  Without k_prev
-    (no previous draft) it is kda_spec_verify.  u may be u_prev itself when
-    both drafts have the same length.  Returns (o, u)."""
+def _spec_step(entry, q, k, v, g, beta, state, state_idx, k_prev, g_prev,
+               u_prev, accepted_prev, scale, o, u):
     lib = load()
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -715,9 +716,13 @@ def kda_spec_step(q, k, v, g, beta, state, *, k_prev=None, g_prev=None,
                          (k, "k", (B, T, H, Dk), q.dtype),
                          (v, "v", (B, T, H, Dv), q.dtype),
                          (g, "g", (B, T, H, Dk), torch.float32),
-                         (beta, "beta", (B, T, H), torch.float32),
-                         (state, "state", (B, H, Dk, Dv), torch.float32)):
+                         (beta, "beta", (B, T, H), torch.float32)):
         _check(t, n, s_, dt, dev)
+    slots = state.shape[0]
+    _check(state, "state", (slots if state_idx is not None else B, H, Dk, Dv),
+           torch.float32, dev)
+    if state_idx is not None:
+        _check(state_idx, "state_idx", (B,), torch.int32, dev)
     T_prev = 0
     if k_prev is not None:
         T_prev = k_prev.shape[1]
@@ -737,13 +742,43 @@ def kda_spec_step(q, k, v, g, beta, state, *, k_prev=None, g_prev=None,
     if u is None:
         u = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
     _check(u, "u", (B, T, H, Dv), torch.float32, dev)
-    st = lib.kda_spec_step(
-        _ptr(k_prev), _ptr(g_prev), _ptr(u_prev), _ptr(accepted_prev), T_prev,
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
-        _ptr(u), B, T, H, Dk, Dv, scale, _dtype_code(q), _stream(dev))
+    head = (_ptr(k_prev), _ptr(g_prev), _ptr(u_prev), _ptr(accepted_prev),
+            T_prev, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta))
+    tail = (B, T, H, Dk, Dv, scale, _dtype_code(q), _stream(dev))
+    if state_idx is None:
+        st = lib.kda_spec_step(*head, _ptr(state), _ptr(o), _ptr(u), *tail)
+    else:
+        st = lib.kda_spec_step_indexed(*head, _ptr(state), _ptr(state_idx),
+                                       slots, _ptr(o), _ptr(u), *tail)
     if st != KDA_OK:
-        raise KDAError("kda_spec_step", st)
+        raise KDAError(entry, st)
     return o, u
+
+
+def kda_spec_step(q, k, v, g, beta, state, *, k_prev=None, g_prev=None,
+                  u_prev=None, accepted_prev=None, scale: float = 1.0,
+                  o=None, u=None):
+    """Commit the previous draft's accepted prefix to `state` (in place) and
+    verify the new draft from the updated state, in one pass over the state:
+    kda_spec_commit(k_prev, g_prev, u_prev, accepted_prev, state) followed by
+    kda_spec_verify(q, k, v, g, beta, state), bit for bit.  Without k_prev
+    (no previous draft) it is kda_spec_verify; with a draft of T = 0 tokens
+    (q of shape [B, 0, H, Dk]) it is kda_spec_commit.  u may be u_prev
+    itself when both drafts have the same length.  Returns (o, u)."""
+    return _spec_step("kda_spec_step", q, k, v, g, beta, state, None, k_prev,
+                      g_prev, u_prev, accepted_prev, scale, o, u)
+
+
+def kda_spec_step_indexed(q, k, v, g, beta, state_pool, state_idx, *,
+                          k_prev=None, g_prev=None, u_prev=None,
+                          accepted_prev=None, scale: float = 1.0, o=None,
+                          u=None):
+    """kda_spec_step with the states in a pool: sequence b uses row
+    state_idx[b] (device int32 [B]) of state_pool [slots, H, Dk, Dv]; a slot
+    outside [0, slots) is padding.  Returns (o, u)."""
+    return _spec_step("kda_spec_step_indexed", q, k, v, g, beta, state_pool,
+                      state_idx, k_prev, g_prev, u_prev, accepted_prev, scale,
+                      o, u)
 
 
 def kda_output_norm_gate(o, z, w, *, eps: float = 1e-6, y=None):
@@ -798,6 +833,39 @@ def kda_decode_step_gated(q, k, v, g, beta, state, z, w, *,
         _stream(dev))
     if st != KDA_OK:
         raise KDAError("kda_decode_step_gated", st)
+    return y
+
+
+def kda_decode_step_gated_indexed(q, k, v, g, beta, state_pool, state_idx, z,
+                                  w, *, eps: float = 1e-6, scale: float = 1.0,
+                                  y=None):
+    """kda_decode_step_gated with the states in a pool (as
+    kda_decode_step_indexed).  Returns y [B, H, Dv]."""
+    lib = load()
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    slots = state_pool.shape[0]
+    for t, n, s_, dt in ((q, "q", (B, H, Dk), q.dtype),
+                         (k, "k", (B, H, Dk), q.dtype),
+                         (v, "v", (B, H, Dv), q.dtype),
+                         (g, "g", (B, H, Dk), torch.float32),
+                         (beta, "beta", (B, H), torch.float32),
+                         (state_pool, "state_pool", (slots, H, Dk, Dv),
+                          torch.float32),
+                         (state_idx, "state_idx", (B,), torch.int32),
+                         (z, "z", (B, H, Dv), q.dtype),
+                         (w, "w", (Dv,), torch.float32)):
+        _check(t, n, s_, dt, dev)
+    if y is None:
+        y = torch.empty((B, H, Dv), dtype=q.dtype, device=dev)
+    _check(y, "y", (B, H, Dv), q.dtype, dev)
+    st = lib.kda_decode_step_gated_indexed(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+        _ptr(state_idx), slots, _ptr(z), _ptr(w), eps, _ptr(y), B, H, Dk, Dv,
+        scale, _dtype_code(q), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_decode_step_gated_indexed", st)
     return y
 
 

@@ -39,6 +39,8 @@ def test_exports_every_declared_symbol():
                           "kda_decode_step", "kda_decode_step_indexed",
                           "kda_prefill_varlen_indexed", "kda_spec_verify",
                           "kda_spec_commit", "kda_spec_step",
+                          "kda_spec_step_indexed",
+                          "kda_decode_step_gated_indexed",
                           "kda_output_norm_gate",
                           "kda_decode_step_gated",
                           "kda_prefill_varlen_prologue",
@@ -356,7 +358,7 @@ def test_spec_step_validation():
     checks, the previous draft's pointers when T_prev > 0, and u reusing
     u_prev's buffer with another draft length."""
     lib = kda.load()
-    assert _step(lib, T=0) == INVALID
+    assert _step(lib, T=-1) == INVALID
     assert _step(lib, T=17) == UNSUP
     assert _step(lib, Tp=17) == UNSUP
     assert _step(lib, Tp=-1) == INVALID
@@ -372,6 +374,11 @@ def test_spec_step_validation():
     # then launch, so only a failing verify check is exercised here
     assert _step(lib, Tp=0, kp=NULL, gp=NULL, up=NULL, accp=NULL,
                  T=17) == UNSUP
+    # neither a previous nor a new draft: nothing to do, nothing enqueued
+    assert _step(lib, Tp=0, T=0, q=NULL, kp=NULL) == OK
+    # no new draft (commit only): the new draft's pointers are not needed,
+    # but the previous draft's still are
+    assert _step(lib, T=0, q=NULL, u=NULL, kp=NULL) == INVALID
 
 
 def _dec_idx(lib, **kw):
@@ -396,6 +403,29 @@ def _pre_idx(lib, **kw):
         a["ws_bytes"], a["stream"])
 
 
+def _step_idx(lib, **kw):
+    a = dict(kp=P, gp=P, up=ctypes.c_void_p(0x200000), accp=P, Tp=4, q=P,
+             k=P, v=P, g=P, beta=P, pool=P, idx=P, slots=4, o=P, u=P, B=2,
+             T=4, H=2, Dk=128, Dv=128, scale=1.0, dtype=0, stream=NULL)
+    a.update(kw)
+    return lib.kda_spec_step_indexed(
+        a["kp"], a["gp"], a["up"], a["accp"], a["Tp"], a["q"], a["k"],
+        a["v"], a["g"], a["beta"], a["pool"], a["idx"], a["slots"], a["o"],
+        a["u"], a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["scale"],
+        a["dtype"], a["stream"])
+
+
+def _gdec_idx(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, pool=P, idx=P, slots=4, z=P, w=P,
+             eps=1e-6, y=P, B=2, H=2, Dk=128, Dv=128, scale=1.0, dtype=0,
+             stream=NULL)
+    a.update(kw)
+    return lib.kda_decode_step_gated_indexed(
+        a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"], a["idx"],
+        a["slots"], a["z"], a["w"], a["eps"], a["y"], a["B"], a["H"],
+        a["Dk"], a["Dv"], a["scale"], a["dtype"], a["stream"])
+
+
 def test_indexed_validation():
     """The state-pool forms check the pool's own arguments first, then
     everything the plain calls check (nothing is launched)."""
@@ -415,6 +445,16 @@ def test_indexed_validation():
     assert _pre_idx(lib, N=0) == INVALID
     assert _pre_idx(lib, C=8) == UNSUP
     assert _pre_idx(lib, ws_bytes=10) == WS
+    assert _step_idx(lib, slots=0) == INVALID
+    assert _step_idx(lib, idx=NULL) == INVALID
+    assert _step_idx(lib, T=17) == UNSUP
+    assert _step_idx(lib, kp=NULL) == INVALID
+    assert _step_idx(lib, Tp=0, T=0) == OK        # nothing enqueued
+    assert _gdec_idx(lib, slots=-2) == INVALID
+    assert _gdec_idx(lib, idx=MIS) == INVALID
+    assert _gdec_idx(lib, z=NULL) == INVALID
+    assert _gdec_idx(lib, eps=-1.0) == INVALID
+    assert _gdec_idx(lib, Dk=72, Dv=72) == UNSUP
 
 
 def test_spec_validation():

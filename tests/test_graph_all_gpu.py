@@ -7,7 +7,8 @@ and at listed positions, the gated prefill on both of its paths (fused into
 the recurrence, and plain prefill then the epilogue), the prologue-fused
 prefill, the standalone epilogue, the gated decode step, speculative verify,
 commit and the fused step, the prefill that uses the library's own
-scratch array, and the state-pool forms of prefill and decode.
+scratch array, and the state-pool forms of prefill, decode, gated decode
+and the speculative step.
 Each replay, with eager resets and synchronisations between replays, must
 give the eager calls' results bit for bit."""
 import numpy as np
@@ -126,6 +127,11 @@ def test_graph_of_every_entry_point():
     didx = torch.tensor([(3 * b + 1) % 20 for b in range(pd.B)],
                         dtype=torch.int32, device=U.DEV)
     od_idx = torch.empty_like(dv)
+    yd_idx = torch.empty_like(dv)
+    spool0 = torch.randn((9,) + tuple(sstate0.shape[1:]), device=U.DEV) * 0.02
+    spool = spool0.clone()
+    sidx = torch.tensor([7, -1, 2, 4], dtype=torch.int32, device=U.DEV)
+    so3, su3 = torch.empty_like(so), torch.empty_like(su)
 
     def varlen_args(x):
         return (x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu"],
@@ -184,10 +190,16 @@ def test_graph_of_every_entry_point():
                                        o=pv_o, workspace=pv_ws)
         kda.kda_decode_step_indexed(dq, dk, dv, dg, dbeta, dpool, didx,
                                     o=od_idx)
+        kda.kda_decode_step_gated_indexed(dq, dk, dv, dg, dbeta, dpool, didx,
+                                          dz, dw, y=yd_idx)
+        kda.kda_spec_step_indexed(sq, sk, sv, sg, sbeta, spool, sidx,
+                                  k_prev=sk, g_prev=sg, u_prev=su,
+                                  accepted_prev=accepted, o=so3, u=su3)
 
     results = [b[key] for b in bufs.values() for key in ("o", "fs", "ck")
                if key in b] + [y_epi, y_dec, dstate, so, su, sstate, so2,
-                               su2, sstate2, pv_o, pv_pool, dpool, od_idx]
+                               su2, sstate2, pv_o, pv_pool, dpool, od_idx,
+                               yd_idx, spool, so3, su3]
 
     def reset():
         for t in results:
@@ -197,6 +209,7 @@ def test_graph_of_every_entry_point():
         sstate2.copy_(sstate0)
         pv_pool.copy_(pv_pool0)
         dpool.copy_(dpool0)
+        spool.copy_(spool0)
 
     reset()
     step()

@@ -1,5 +1,6 @@
-"""GPU tests of the state-pool entry points, kda_decode_step_indexed and
-kda_prefill_varlen_indexed.
+"""GPU tests of the state-pool entry points: kda_decode_step_indexed,
+kda_decode_step_gated_indexed, kda_prefill_varlen_indexed and
+kda_spec_step_indexed.
 
 Their contract is the plain call on the gathered states followed by a
 scatter of the new states, bit for bit (the kernels are the same; only the
@@ -169,3 +170,76 @@ def test_prefill_then_decode_from_the_pool_against_the_oracle():
     # rows no request uses are untouched
     for r in set(range(slots)) - set(idx):
         assert np.array_equal(U.host(pool)[r], pool_host[r].astype(np.float32))
+
+
+def test_gated_decode_indexed_equals_gather_scatter():
+    B, H, D, slots = 10, 6, 128, 24
+    rng = np.random.default_rng(33)
+    d = inputs.make("decode", seed=34, B=B, H=H)
+    q, k, v = (U.to_dev(x, d.dtype) for x in (d.q, d.k, d.v))
+    g, beta = U.f32_dev(d.g), U.f32_dev(d.beta)
+    z = U.to_dev(rng.standard_normal((B, H, D)).astype(np.float32), "bf16")
+    w = U.f32_dev((0.5 + rng.random(D)).astype(np.float32))
+    pool = _pool(rng, slots, H, D, D)
+    idx = [int(x) for x in rng.permutation(slots)[:B]]
+    idx[2] = -1
+    sidx = torch.tensor(idx, dtype=torch.int32, device=U.DEV)
+    valid = [b for b in range(B) if idx[b] >= 0]
+    gathered = torch.zeros((B, H, D, D), dtype=torch.float32, device=U.DEV)
+    for b in valid:
+        gathered[b] = pool[idx[b]]
+    y_ref = kda.kda_decode_step_gated(q, k, v, g, beta, gathered, z, w)
+    pool_ref = pool.clone()
+    for b in valid:
+        pool_ref[idx[b]] = gathered[b]
+    y = kda.kda_decode_step_gated_indexed(q, k, v, g, beta, pool, sidx, z, w)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref) and torch.equal(pool, pool_ref)
+
+
+@pytest.mark.parametrize("Tp,T", [(4, 4), (3, 6), (5, 0), (0, 2)])
+def test_spec_step_indexed_equals_gather_scatter(Tp, T):
+    """The fused speculative step on pooled states (a padding entry, mixed
+    acceptance), against the step on gathered states: commit and verify,
+    commit only (T = 0) and verify only (T_prev = 0)."""
+    B, H, D, slots = 6, 5, 64, 16
+    rng = np.random.default_rng(50 + Tp + 7 * T)
+
+    def draft(seed, n):
+        if n == 0:
+            z = lambda *s: torch.zeros(s, device=U.DEV)  # noqa: E731
+            return (z(B, 0, H, D).to(torch.bfloat16),
+                    z(B, 0, H, D).to(torch.bfloat16),
+                    z(B, 0, H, D).to(torch.bfloat16), z(B, 0, H, D),
+                    z(B, 0, H))
+        p = inputs.make("varlen", seed=seed, H=H, K=D, V=D, lengths=[n] * B)
+        shp = lambda x: x.reshape((B, n) + x.shape[1:])  # noqa: E731
+        q, k, v = (U.to_dev(shp(x), p.dtype) for x in (p.q, p.k, p.v))
+        return q, k, v, U.f32_dev(shp(p.g)), U.f32_dev(shp(p.beta))
+    new = draft(60 + T, T)
+    pool = _pool(rng, slots, H, D, D)
+    idx = [int(x) for x in rng.permutation(slots)[:B]]
+    idx[4] = slots + 2                            # padding
+    sidx = torch.tensor(idx, dtype=torch.int32, device=U.DEV)
+    valid = [b for b in range(B) if 0 <= idx[b] < slots]
+    gathered = torch.zeros((B, H, D, D), dtype=torch.float32, device=U.DEV)
+    for b in valid:
+        gathered[b] = pool[idx[b]]
+    kw = {}
+    if Tp:
+        prev = draft(70 + Tp, Tp)
+        _, u_prev = kda.kda_spec_verify(*prev, gathered)
+        acc = torch.tensor([int(a) for a in rng.integers(0, Tp + 1, B)],
+                           dtype=torch.int32, device=U.DEV)
+        kw = dict(k_prev=prev[1], g_prev=prev[3], u_prev=u_prev,
+                  accepted_prev=acc)
+    st_ref = gathered.clone()
+    o_ref, u_ref = kda.kda_spec_step(*new, st_ref, **kw)
+    pool_ref = pool.clone()
+    for b in valid:
+        pool_ref[idx[b]] = st_ref[b]
+    o, u = kda.kda_spec_step_indexed(*new, pool, sidx, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(pool, pool_ref), "pool rows"
+    if T:
+        assert torch.equal(o, o_ref) and torch.equal(u, u_ref)

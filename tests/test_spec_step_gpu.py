@@ -178,3 +178,20 @@ def test_step_at_the_decode_workload():
     torch.cuda.synchronize()
     assert torch.equal(st_a, st_b)
     assert torch.equal(o_a, o_b) and torch.equal(u_a, u_b)
+
+
+def test_step_without_new_draft_is_commit():
+    """T = 0 (no new draft): the step is the commit alone, bit for bit."""
+    B, H, T = 5, 4, 6
+    p0, prev = draft(750, B, T, H, 128, 128, "bf16")
+    s0 = U.f32_dev(p0.initial_state)
+    accepted = torch.tensor([0, 6, 3, 9, 1], dtype=torch.int32, device=U.DEV)
+    _, u_prev = kda.kda_spec_verify(*prev, s0)
+    st_a = s0.clone()
+    kda.kda_spec_commit(prev[1], prev[3], u_prev, accepted, st_a)
+    empty = tuple(x[:, :0] for x in prev)
+    st_b = s0.clone()
+    kda.kda_spec_step(*empty, st_b, k_prev=prev[1], g_prev=prev[3],
+                      u_prev=u_prev, accepted_prev=accepted)
+    torch.cuda.synchronize()
+    assert torch.equal(st_a, st_b)
