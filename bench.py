@@ -207,17 +207,17 @@ def main(argv=None):
                     help="run the prefill through kda_prefill_varlen_ckpt, "
                          "storing the state every N tokens (a multiple of "
                          "the chunk size)")
-    ap.add_argument("--spec-tokens", type=int, default=0,
-                    help="also time speculative verify + commit of this many "
-                         "draft tokens per sequence on the decode batch "
-                         "(outside the timed steps)")
+    ap.add_argument("--spec-tokens", type=int, default=4,
+                    help="time speculative verify, commit and the fused step "
+                         "with this many draft tokens per sequence on the "
+                         "decode batch (outside the timed steps; 0 skips)")
     ap.add_argument("--no-epilogue", action="store_true",
                     help="skip timing the output epilogue (standalone over "
                          "the prefill output, fused into the prefill's "
                          "recurrence, fused into the decode step), taken "
                          "after the timed steps")
-    ap.add_argument("--prologue", action="store_true",
-                    help="also time the prefill with the input prologue "
+    ap.add_argument("--no-prologue", dest="prologue", action="store_false",
+                    help="skip timing the prefill with the input prologue "
                          "fused (outside the timed steps)")
     ap.add_argument("--step-only", action="store_true",
                     help="skip the measurements taken after the timed steps "
