@@ -226,3 +226,68 @@ def test_random_prologue(seed):
     s0 = bool(rng.random() < 0.7)
     PR.check(PR.make_case(600 + seed, lengths, H, D, C, dtype, s0),
              "random case %d" % seed, rounded_ref=True)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_state_pools(seed):
+    """kda_prefill_varlen_indexed then kda_decode_step_indexed on random
+    sizes, pool sizes, slot maps (with padding entries) and new requests,
+    against the plain calls on gathered states and a scatter, bit for bit."""
+    import torch
+    from linear_recurrent_attention_kda_amd import kda
+    rng = np.random.default_rng(1000 + seed)
+    dims = [16 * i for i in range(1, 9)]
+    Dk, Dv = int(rng.choice(dims)), int(rng.choice(dims))
+    H = int(rng.choice([1, 3, 8, 70]))
+    n = int(rng.integers(1, 7))
+    lengths = [int(x) for x in rng.integers(0, 300, size=n)]
+    C = int(rng.choice([16, 32, 64]))
+    dtype = "bf16" if rng.random() < 0.75 else "fp32"
+    slots = n + int(rng.integers(0, 6))
+    idx = [int(x) for x in rng.permutation(slots)[:n]]
+    for i in range(n):
+        if rng.random() < 0.2:
+            idx[i] = int(rng.choice([-1, slots, slots + 5]))
+    has = [int(rng.random() < 0.7) for _ in range(n)]
+    U.log("random pools %d: Dk=%d Dv=%d H=%d C=%d %s lengths=%s slots=%d "
+          "idx=%s has=%s" % (seed, Dk, Dv, H, C, dtype, lengths, slots, idx,
+                             has))
+    p = inputs.make("varlen", seed=1100 + seed, H=H, K=Dk, V=Dv, C=C,
+                    dtype=dtype, lengths=lengths)
+    q, k, v = (U.to_dev(x, p.dtype) for x in (p.q, p.k, p.v))
+    g, beta = U.f32_dev(p.g), U.f32_dev(p.beta)
+    cu = torch.from_numpy(p.cu_seqlens).to(U.DEV)
+    maxlen = max(1, max(lengths))
+    pool = torch.from_numpy((rng.standard_normal((slots, H, Dk, Dv)) * 0.02)
+                            .astype(np.float32)).to(U.DEV)
+    sidx = torch.tensor(idx, dtype=torch.int32, device=U.DEV)
+    valid = [i for i in range(n) if 0 <= idx[i] < slots]
+    s0 = torch.zeros((n, H, Dk, Dv), dtype=torch.float32, device=U.DEV)
+    for i in valid:
+        if has[i]:
+            s0[i] = pool[idx[i]]
+    o_ref, fs = kda.kda_prefill_varlen(q, k, v, g, beta, cu, maxlen, s0,
+                                       chunk_size=C)
+    pool_ref = pool.clone()
+    for i in valid:
+        pool_ref[idx[i]] = fs[i]
+    o = kda.kda_prefill_varlen_indexed(
+        q, k, v, g, beta, cu, maxlen, pool, sidx,
+        torch.tensor(has, dtype=torch.int32, device=U.DEV), chunk_size=C)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(pool, pool_ref)
+    # a decode step for the same requests from the pool
+    d = inputs.make("decode", seed=1200 + seed, B=n, H=H, K=Dk, V=Dv,
+                    dtype=dtype)
+    dq, dk, dv = (U.to_dev(x, d.dtype) for x in (d.q, d.k, d.v))
+    dg, db = U.f32_dev(d.g), U.f32_dev(d.beta)
+    st = torch.zeros((n, H, Dk, Dv), dtype=torch.float32, device=U.DEV)
+    for i in valid:
+        st[i] = pool[idx[i]]
+    od_ref = kda.kda_decode_step(dq, dk, dv, dg, db, st)
+    pool_ref = pool.clone()
+    for i in valid:
+        pool_ref[idx[i]] = st[i]
+    od = kda.kda_decode_step_indexed(dq, dk, dv, dg, db, pool, sidx)
+    torch.cuda.synchronize()
+    assert torch.equal(od, od_ref) and torch.equal(pool, pool_ref)
