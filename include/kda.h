@@ -92,10 +92,11 @@ int32_t kda_abi_version(void);
 const char* kda_status_string(int32_t status);
 
 /*
- * Bytes of device workspace that the prefill entry points (kda_prefill_chunked,
- * kda_prefill_varlen and its _ckpt, _ckpt_at, _gated, _prologue, _indexed,
- * _prep and _recur forms; _noalloc holds it internally) need for N sequences holding
- * total_T tokens (fixed length: N = B, total_T = B*T).  The workspace holds, per head and chunk, the chunk-prep
+ * Bytes of device workspace that the prefill entry points need
+ * (kda_prefill_chunked, and kda_prefill_varlen with its _ckpt, _ckpt_at,
+ * _gated, _prologue, _indexed, _prep and _recur forms; _noalloc holds it
+ * internally) for N sequences holding total_T tokens (fixed length: N = B,
+ * total_T = B*T).  The workspace holds, per head and chunk, the chunk-prep
  * kernel's outputs that the chunk-recurrence kernel consumes ("FlashKDA
  * algorithm": K1 prepares chunk tensors in parallel, K2 runs the chunk-level
  * recurrence).  Returns 0 for unsupported sizes.
