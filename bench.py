@@ -631,9 +631,8 @@ def _clock_entries(node, path=""):
 def gpu_clocks(busy=None):
     """The GPU's clocks as its kernel driver reports them (amd-smi, else
     rocm-smi: read-only queries, nothing is pinned or changed), read while
-    `busy()`
-    keeps the GPU working, so that the figures are the loaded clocks rather
-    than idle ones.  Returns the current gfx clock of each XCD, the memory
+    `busy()` keeps the GPU working, so that the figures are the loaded
+    clocks rather than idle ones.  Returns the current gfx clock of each XCD, the memory
     clock, the gfx maximum and whether clocks are locked; the raw text when
     the report is not JSON; or None."""
     import subprocess
