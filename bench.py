@@ -632,9 +632,9 @@ def gpu_clocks(busy=None):
     """The GPU's clocks as its kernel driver reports them (amd-smi, else
     rocm-smi: read-only queries, nothing is pinned or changed), read while
     `busy()` keeps the GPU working, so that the figures are the loaded
-    clocks rather than idle ones.  Returns the current gfx clock of each XCD, the memory
-    clock, the gfx maximum and whether clocks are locked; the raw text when
-    the report is not JSON; or None."""
+    clocks rather than idle ones.  Returns the current gfx clock of each
+    XCD, the memory clock, the gfx maximum and whether clocks are locked;
+    the raw text when the report is not JSON; or None."""
     import subprocess
     for cmd in (["amd-smi", "metric", "-g", "0", "-c", "--json"],
                 ["rocm-smi", "-d", "0", "--showclocks", "--json"]):
