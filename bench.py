@@ -17,8 +17,9 @@ kda_prefill_varlen_recur), so that each of the step's three kernels is timed
 on its own; `kernels` gives each one's algorithmic HBM rate against the
 peak, and `roofline` repeats the one that takes the largest share of the
 step.  Kernel durations come from HIP events on the stream the kernels run
-on, created without the system-scope fence (see HipEvent).  Decode rotates three state buffers so that consecutive steps never
-find the state in the 256 MB Infinity Cache.
+on, created without the system-scope fence (see HipEvent).  Decode rotates
+three state buffers so that consecutive steps never find the state in the
+256 MB Infinity Cache.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
