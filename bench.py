@@ -922,7 +922,7 @@ def time_gated_prefill(ins, cu, maxlen, total, H, K, V, C, s0, ws, dev,
     recurrence when there are at least two (sequence, head) pairs per
     compute unit, else the plain recurrence then the epilogue kernel),
     against the plain prefill followed by kda_output_norm_gate; each n
-    launches back to back between two events, the faster of two rounds."""
+    launches back to back between two events, the fastest of four rounds."""
     import torch
     from linear_recurrent_attention_kda_amd import kda
     q, k, v, g, beta = ins
@@ -953,18 +953,23 @@ def time_gated_prefill(ins, cu, maxlen, total, H, K, V, C, s0, ws, dev,
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
-    # Both paths warmed up, then timed alternately in two rounds, keeping
-    # each path's faster round: whichever is timed first otherwise pays for
-    # the clock and cache state the previous legs left behind (measured up
-    # to 12 % on the 8K-token prefill).
+    # Both paths warmed up, then timed alternately in four rounds, each path
+    # first in every other round, keeping each path's fastest round:
+    # whichever is timed first otherwise pays for the clock and cache state
+    # the previous legs left behind (measured up to 12 % on the 8K-token
+    # prefill).
     for _ in range(3):
         gated()
         two_pass()
     torch.cuda.synchronize()
     t_g = t_2 = float("inf")
-    for _ in range(2):
-        t_g = min(t_g, timed(gated))
-        t_2 = min(t_2, timed(two_pass))
+    for r in range(4):
+        if r % 2 == 0:
+            t_g = min(t_g, timed(gated))
+            t_2 = min(t_2, timed(two_pass))
+        else:
+            t_2 = min(t_2, timed(two_pass))
+            t_g = min(t_g, timed(gated))
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     path = "fused" if nseq * H >= 2 * cus else "two-pass"
     log("gated prefill (%s): %.4f ms; plain + epilogue %.4f ms"
